@@ -1,0 +1,176 @@
+/*
+ * paged_decode.h -- C ABI of libpaged_decode.so: split-KV paged decode
+ * attention for MI355X (gfx950).
+ *
+ * One decode step of an LLM inference engine: a batch of B single-token
+ * queries attends over a paged bf16 KV cache.  The operations follow the
+ * AstrAI engine as described on three commit pages:
+ *   [WS] AstrAI commit 0b661bae, astrai/inference/core/workspace.py view
+ *   [CA] AstrAI commit cbc58447, astrai/inference/core/cache.py view
+ *   [EX] AstrAI commit e0f7fa8e, astrai/inference/core/executor.py view
+ *
+ * Conventions for every entry point:
+ *   - Returns a pd_status; nothing aborts, throws or prints.
+ *   - Every device pointer is borrowed: the caller allocates and frees it
+ *     (typically with PyTorch).  Device pointers must be 16-byte aligned.
+ *   - The library never calls hipMalloc/hipFree.  All per-step buffers live in
+ *     one caller-supplied device arena carved at fixed offsets at init, so the
+ *     kernel arguments of a step never change and a whole multi-layer step can
+ *     be captured into a hipGraph and replayed ([WS]: buffers preallocated at
+ *     executor init, no allocation in the decode hot loop, fixed addresses as
+ *     the prerequisite for graph capture).
+ *   - Work is enqueued on the given stream only; no call except
+ *     paged_decode_read_error reads device memory back or synchronises.
+ *   - A handle is not thread-safe; use one per thread or serialise.
+ *   - Identical inputs and split count give bit-identical results.
+ *
+ * Index conventions (all int32): kv_indptr and kv_indices are token-granular.
+ * Page p owns storage slots [p*page_size, (p+1)*page_size).  A request's t-th
+ * cached token is in page req_to_page[b][t / page_size] at offset
+ * t % page_size.  Query head h reads kv head h / (n_heads / n_kv_heads).
+ */
+#ifndef PAGED_DECODE_H
+#define PAGED_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pd_status {
+  PD_OK = 0,
+  PD_E_INVALID = 1,     /* null / misaligned pointer, bad dimension or mode   */
+  PD_E_UNSUPPORTED = 2, /* head_dim not 64/128, n_heads % n_kv_heads != 0,
+                           group size above 16 ([EX]: graphs only for a
+                           supported head_dim)                                */
+  PD_E_CAPACITY = 3,    /* batch > max_batch, splits > max_splits, arena too
+                           small, layer out of range                          */
+  PD_E_HIP = 4          /* a HIP launch or copy failed                        */
+} pd_status;
+
+/* Bits of the device error word (see paged_decode_read_error).  A kernel that
+ * meets a bad value records it here and clamps instead of reading out of
+ * bounds; outputs of a step with a nonzero word are undefined. */
+enum {
+  PD_ERR_NEG_SEQ_LEN = 1u << 0,    /* seq_lens[b] < 0: treated as 0          */
+  PD_ERR_SEQ_OVER_TABLE = 1u << 1, /* seq_lens[b] > max_pages_per_req*page_size:
+                                      clamped to that                          */
+  PD_ERR_TOTAL_OVER_CAP = 1u << 2, /* sum(seq_lens) > max_total_tokens: the
+                                      lengths are clipped to fit               */
+  PD_ERR_BAD_PAGE = 1u << 3        /* a page id outside [0, num_slots/page_size):
+                                      its slots are redirected to slot 0       */
+};
+
+/* Bind modes ([CA]: steady-state detection lets bind increment seq_lens and
+ * kv_indptr in place and reuse the request map; [WS]: position_ids, seq_lens
+ * and kv_indptr are updated in place instead of rebuilt). */
+enum {
+  PD_BIND_FULL = 0,   /* the caller has written seq_lens for this step        */
+  PD_BIND_STEADY = 1  /* same requests, each one token longer: the device adds
+                         1 to seq_lens[b] and position_ids[b] first           */
+};
+
+typedef struct pd_config {
+  int32_t n_layers;          /* layers in the K/V stores                        */
+  int32_t n_heads;           /* query heads H                                   */
+  int32_t n_kv_heads;        /* kv heads Hkv; H % Hkv == 0, H / Hkv <= 16       */
+  int32_t head_dim;          /* D: 64 or 128                                    */
+  int32_t page_size;         /* tokens per page, >= 1                           */
+  int32_t max_batch;         /* 1 .. 1024                                       */
+  int32_t max_splits;        /* 1 .. 256: capacity of the split partials        */
+  int32_t max_pages_per_req; /* row width of req_to_page, >= 1                  */
+  int64_t num_slots;         /* slots per layer in each store, >= page_size     */
+  int64_t max_total_tokens;  /* capacity of kv_indices (sum of seq_lens), >= 1  */
+} pd_config;
+
+/* Byte offsets into the arena and the shapes behind them. */
+typedef struct pd_layout {
+  size_t arena_bytes;
+  size_t kv_indptr;   /* int32 [max_batch + 1]                                 */
+  size_t kv_indices;  /* int32 [max_total_tokens]                              */
+  size_t o_part;      /* fp32  [max_batch, n_heads, max_splits, head_dim]:
+                         each split's output normalised by its own softmax sum
+                         ([WS] decode_o_part)                                  */
+  size_t ml_part;     /* fp32  [max_batch, n_heads, max_splits, 2]: (m, ln l)
+                         with m the split's max scaled score and
+                         l = sum exp(s - m); lse = m + ln l; an empty split
+                         holds (-inf, -inf) ([WS] decode_ml_part)              */
+  size_t meta;        /* int32 [16]: [0] = max pages of any request this step,
+                         [1] = total tokens this step                          */
+  size_t error_word;  /* uint32: PD_ERR_* bits                                 */
+} pd_layout;
+
+typedef struct pd_handle pd_handle;
+
+/* Arena size for a config (pure host).  Every sub-buffer is 256-byte aligned. */
+pd_status paged_decode_workspace_bytes(const pd_config* cfg, size_t* bytes);
+
+/* Validates cfg and carves the caller's device arena (d_arena, arena_bytes >=
+ * paged_decode_workspace_bytes) at fixed offsets.  Allocates only the small
+ * host handle; never device memory.  The arena must stay alive and untouched
+ * by the caller (except through read-only views) until destroy.  Zeroes the
+ * error word with a blocking copy on the null stream. */
+pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena,
+                                      size_t arena_bytes, pd_handle** out);
+
+/* Offsets of the arena's sub-buffers, for read-only views (tests, tools). */
+pd_status paged_decode_layout(const pd_handle* h, pd_layout* out);
+
+/* Resolves the split count S for a batch: requested > 0 is honoured (it must be
+ * <= max_splits); requested == 0 picks one from batch x n_kv_heads against the
+ * device's compute units (and max_pages_per_req, so a split keeps >= 4 pages).
+ * Pass the same S to paged_decode_attn and paged_decode_merge. */
+pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t requested,
+                                  int32_t* num_splits);
+
+/* Per-step metadata ([CA]: kv_indptr is the prefix sum of seq_lens, built once
+ * per step and shared by every layer; steady +1 update).
+ *   d_seq_lens      int32 [batch], in/out (incremented in PD_BIND_STEADY)
+ *   d_position_ids  int32 [batch], in/out (incremented in PD_BIND_STEADY; may
+ *                   be NULL in PD_BIND_FULL)
+ *   d_req_to_page   int32 [batch, max_pages_per_req] row-major page ids
+ * Writes the arena's kv_indptr [batch+1] and kv_indices [sum seq_lens] and the
+ * meta words.  Two kernels on `stream`; no host sync. */
+pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
+                            int32_t* d_position_ids, const int32_t* d_req_to_page,
+                            hipStream_t stream);
+
+/* Split-KV attention for one layer ([WS]: attn_paged_decode writes split
+ * partials into decode_o_part / decode_ml_part).
+ *   d_q        bf16 [batch, n_heads, head_dim] queries of this layer
+ *   d_k_store  bf16 [n_layers, num_slots, n_kv_heads, head_dim] (base of the
+ *   d_v_store  whole store; the library adds the 64-bit offset of `layer`)
+ *   scale      softmax scale applied to q.k (float32)
+ * Split j of request b covers pages [j*c, (j+1)*c) with
+ * c = max(1, ceil(max_b ceil(L_b/page_size) / S)); splits past a request's end
+ * are written as empty.  Reads kv_indptr / kv_indices from the last bind. */
+pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
+                            const void* d_q, const void* d_k_store, const void* d_v_store,
+                            float scale, hipStream_t stream);
+
+/* Log-sum-exp merge of the S partials into decode_out ([WS]: decode_out is
+ * preallocated in the workspace):
+ *   out[b,h,:] = sum_j exp(lse_j - LSE) o_j,  LSE = log sum_j exp(lse_j),
+ * empty splits skipped, rounded to bf16 (nearest-even).  A request with no
+ * tokens gets zeros.  d_out bf16 [batch, n_heads, head_dim], caller-owned. */
+pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
+                             hipStream_t stream);
+
+/* Diagnostics, never in the hot path: synchronises `stream`, returns the
+ * device error word (PD_ERR_* bits) and clears it. */
+pd_status paged_decode_read_error(pd_handle* h, uint32_t* flags, hipStream_t stream);
+
+/* Frees the host handle; the arena belongs to the caller. */
+pd_status paged_decode_destroy(pd_handle* h);
+
+/* Static description of a status code. */
+const char* paged_decode_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_DECODE_H */

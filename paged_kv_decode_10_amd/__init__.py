@@ -1,0 +1,192 @@
+"""Split-KV paged decode attention for MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libpaged_decode.so``
+(``include/paged_decode.h``): it only checks and marshals arguments (torch
+tensors -> device pointers, torch streams -> hipStream_t).  Every step of the
+decode path runs in the library's HIP kernels; nothing here computes.
+
+    ws = PagedDecode(Config(...), device="cuda")
+    S = ws.num_splits(batch)
+    ws.bind(batch, PD_BIND_FULL, seq_lens, position_ids, req_to_page)
+    for layer in range(n_layers):
+        ws.attn(batch, layer, S, q[layer], k_store, v_store, scale)
+        ws.merge(batch, S, out[layer])
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+from ._abi import (  # noqa: F401
+    PD_BIND_FULL,
+    PD_BIND_STEADY,
+    PD_E_CAPACITY,
+    PD_E_HIP,
+    PD_E_INVALID,
+    PD_E_UNSUPPORTED,
+    PD_ERR_BAD_PAGE,
+    PD_ERR_NEG_SEQ_LEN,
+    PD_ERR_SEQ_OVER_TABLE,
+    PD_ERR_TOTAL_OVER_CAP,
+    PD_OK,
+    PagedDecodeError,
+)
+
+__all__ = ["Config", "PagedDecode", "PagedDecodeError", "PD_BIND_FULL", "PD_BIND_STEADY",
+           "workspace_bytes", "library_path"]
+
+
+def library_path() -> str:
+    return _abi.LIB_PATH
+
+
+@dataclass
+class Config:
+    n_layers: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    page_size: int
+    max_batch: int
+    max_splits: int
+    max_pages_per_req: int
+    num_slots: int
+    max_total_tokens: int
+
+    def to_c(self) -> _abi.PdConfig:
+        return _abi.PdConfig(self.n_layers, self.n_heads, self.n_kv_heads, self.head_dim,
+                             self.page_size, self.max_batch, self.max_splits,
+                             self.max_pages_per_req, self.num_slots, self.max_total_tokens)
+
+
+def workspace_bytes(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.to_c()
+    _abi.check("paged_decode_workspace_bytes",
+               _abi.lib().paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dev_ptr(t: torch.Tensor, dtype, name: str, numel: int | None = None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+class PagedDecode:
+    """One workspace: a device arena carved by the library, plus its handle."""
+
+    def __init__(self, cfg: Config, device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        L = _abi.lib()
+        nbytes = workspace_bytes(cfg)
+        self.arena = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        c = cfg.to_c()
+        with torch.cuda.device(self.device):
+            _abi.check("paged_decode_init_workspace",
+                       L.paged_decode_init_workspace(ctypes.byref(c), ctypes.c_void_p(self.arena.data_ptr()),
+                                                     nbytes, ctypes.byref(h)))
+        self._h = h
+        lay = _abi.PdLayout()
+        _abi.check("paged_decode_layout", L.paged_decode_layout(self._h, ctypes.byref(lay)))
+        self.layout = {f: getattr(lay, f) for f, _ in _abi.PdLayout._fields_}
+
+    # ---------------------------------------------------------- views -----
+    def _view(self, off: int, dtype, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        return self.arena[off: off + n * itemsize].view(dtype).view(*shape)
+
+    @property
+    def kv_indptr(self):
+        return self._view(self.layout["kv_indptr"], torch.int32, (self.cfg.max_batch + 1,))
+
+    @property
+    def kv_indices(self):
+        return self._view(self.layout["kv_indices"], torch.int32, (self.cfg.max_total_tokens,))
+
+    @property
+    def o_part(self):
+        c = self.cfg
+        return self._view(self.layout["o_part"], torch.float32,
+                          (c.max_batch, c.n_heads, c.max_splits, c.head_dim))
+
+    @property
+    def ml_part(self):
+        c = self.cfg
+        return self._view(self.layout["ml_part"], torch.float32, (c.max_batch, c.n_heads, c.max_splits, 2))
+
+    @property
+    def meta(self):
+        return self._view(self.layout["meta"], torch.int32, (16,))
+
+    # ---------------------------------------------------------- calls -----
+    def num_splits(self, batch: int, requested: int = 0) -> int:
+        s = ctypes.c_int32(0)
+        _abi.check("paged_decode_num_splits",
+                   _abi.lib().paged_decode_num_splits(self._h, batch, requested, ctypes.byref(s)))
+        return int(s.value)
+
+    def bind(self, batch: int, mode: int, seq_lens: torch.Tensor, position_ids, req_to_page: torch.Tensor,
+             stream=None) -> None:
+        c = self.cfg
+        p_sl = _dev_ptr(seq_lens, torch.int32, "seq_lens", batch)
+        p_pos = None if position_ids is None else _dev_ptr(position_ids, torch.int32, "position_ids", batch)
+        p_tab = _dev_ptr(req_to_page, torch.int32, "req_to_page", batch * c.max_pages_per_req)
+        if req_to_page.dim() == 2 and req_to_page.shape[1] != c.max_pages_per_req:
+            raise ValueError("req_to_page rows must have max_pages_per_req entries")
+        _abi.check("paged_decode_bind",
+                   _abi.lib().paged_decode_bind(self._h, batch, mode, p_sl, p_pos, p_tab, _stream_ptr(stream)))
+
+    def attn(self, batch: int, layer: int, num_splits: int, q: torch.Tensor, k_store: torch.Tensor,
+             v_store: torch.Tensor, scale: float, stream=None) -> None:
+        c = self.cfg
+        store_numel = c.n_layers * c.num_slots * c.n_kv_heads * c.head_dim
+        p_q = _dev_ptr(q, torch.bfloat16, "q", batch * c.n_heads * c.head_dim)
+        p_k = _dev_ptr(k_store, torch.bfloat16, "k_store", store_numel)
+        p_v = _dev_ptr(v_store, torch.bfloat16, "v_store", store_numel)
+        _abi.check("paged_decode_attn",
+                   _abi.lib().paged_decode_attn(self._h, batch, layer, num_splits, p_q, p_k, p_v,
+                                                float(scale), _stream_ptr(stream)))
+
+    def merge(self, batch: int, num_splits: int, out: torch.Tensor, stream=None) -> None:
+        c = self.cfg
+        p_o = _dev_ptr(out, torch.bfloat16, "out", batch * c.n_heads * c.head_dim)
+        _abi.check("paged_decode_merge",
+                   _abi.lib().paged_decode_merge(self._h, batch, num_splits, p_o, _stream_ptr(stream)))
+
+    def read_error(self, stream=None) -> int:
+        v = ctypes.c_uint32(0)
+        _abi.check("paged_decode_read_error",
+                   _abi.lib().paged_decode_read_error(self._h, ctypes.byref(v), _stream_ptr(stream)))
+        return int(v.value)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _abi.lib().paged_decode_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,124 @@
+// Per-step bind: the steady +1 update, the kv_indptr prefix sum and the
+// kv_indices slot fill.
+//
+// AstrAI commit cbc58447 (cache.py view): kv_indptr is the prefix sum of
+// seq_lens, built once per decode step and reused by every layer; in the steady
+// state (same requests, one more token each) seq_lens / kv_indptr are advanced
+// in place and position_ids moves by +1 instead of being rebuilt.  The flat
+// kv_indices list is the slot of each cached token, looked up through the
+// request's page list (the request -> token pool of the same page).
+#include "pd_internal.h"
+
+namespace pd {
+namespace {
+
+constexpr int kScanThreads = 1024;  // one thread per request (max_batch <= 1024)
+
+__device__ inline int64_t wave_inclusive_scan(int64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ inline int wave_max_int(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+// One workgroup.  Thread b owns request b.
+__global__ void __launch_bounds__(kScanThreads)
+bind_scan_kernel(BindArgs a) {
+  __shared__ int64_t wave_tot[kScanThreads / 64];
+  __shared__ int wave_maxp[kScanThreads / 64];
+  const int b = threadIdx.x;
+  const int lane = b & 63, wave = b >> 6;
+  uint32_t flags = 0;
+  int64_t len = 0;
+  if (b < a.batch) {
+    int32_t L = a.seq_lens[b];
+    if (a.mode == PD_BIND_STEADY) {
+      L += 1;
+      a.seq_lens[b] = L;
+      if (a.position_ids) a.position_ids[b] += 1;
+    }
+    const int64_t cap = (int64_t)a.max_pages_per_req * a.page_size;
+    len = L;
+    if (len < 0) { len = 0; flags |= PD_ERR_NEG_SEQ_LEN; }
+    if (len > cap) { len = cap; flags |= PD_ERR_SEQ_OVER_TABLE; }
+  }
+  // Block-wide exclusive scan of the lengths (int64: no overflow before the
+  // capacity clip).
+  int64_t incl = wave_inclusive_scan(len);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_tot[w];
+  const int64_t excl = before + incl - len;
+  // Clip to the kv_indices capacity so every later read stays in bounds.
+  const int64_t lo = min(excl, a.max_total_tokens);
+  const int64_t hi = min(excl + len, a.max_total_tokens);
+  if (b < a.batch && hi - lo < len) flags |= PD_ERR_TOTAL_OVER_CAP;
+  const int pages = (int)((hi - lo + a.page_size - 1) / a.page_size);
+  if (b < a.batch) {
+    a.kv_indptr[b + 1] = (int32_t)hi;
+    if (b == 0) a.kv_indptr[0] = 0;
+  }
+  int mp = wave_max_int(b < a.batch ? pages : 0);
+  if (lane == 0) wave_maxp[wave] = mp;
+  __syncthreads();
+  if (b == 0) {
+    int m = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) m = max(m, wave_maxp[w]);
+    a.meta[kMetaMaxPages] = m;
+    int64_t total = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) total += wave_tot[w];
+    a.meta[kMetaTotalTokens] = (int32_t)min(total, a.max_total_tokens);
+  }
+  if (flags) atomicOr(a.error_word, flags);
+}
+
+constexpr int kFillThreads = 256;
+
+// Grid (batch, Y): block (b, y) fills tokens y*256 + tid, stepping 256*Y, of
+// request b.  The token range comes from the (already clipped) kv_indptr.
+__global__ void __launch_bounds__(kFillThreads)
+bind_fill_kernel(BindArgs a) {
+  const int b = blockIdx.x;
+  const int32_t start = a.kv_indptr[b];
+  const int32_t len = a.kv_indptr[b + 1] - start;
+  const int32_t* row = a.req_to_page + (int64_t)b * a.max_pages_per_req;
+  uint32_t flags = 0;
+  for (int32_t t = blockIdx.y * kFillThreads + threadIdx.x; t < len;
+       t += kFillThreads * gridDim.y) {
+    const int32_t page = row[t / a.page_size];
+    int64_t slot;
+    if (page < 0 || (int64_t)page >= a.num_pages) {
+      flags |= PD_ERR_BAD_PAGE;
+      slot = 0;
+    } else {
+      slot = (int64_t)page * a.page_size + t % a.page_size;
+    }
+    a.kv_indices[start + t] = (int32_t)slot;
+  }
+  if (flags) atomicOr(a.error_word, flags);
+}
+
+}  // namespace
+
+hipError_t launch_bind(const BindArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(bind_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t cap = (int64_t)a.max_pages_per_req * a.page_size;
+  int y = (int)((cap + 4 * kFillThreads - 1) / (4 * kFillThreads));
+  y = y < 1 ? 1 : (y > 256 ? 256 : y);
+  hipLaunchKernelGGL(bind_fill_kernel, dim3(a.batch, y), dim3(kFillThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pd

@@ -1,0 +1,257 @@
+// Host side of libpaged_decode.so: config validation, arena carve-up, split
+// heuristic and the extern "C" entry points declared in include/paged_decode.h.
+//
+// AstrAI commit 0b661bae (workspace.py view): every per-step buffer is
+// preallocated once (at executor init) at a fixed address, so nothing in the
+// decode loop allocates and the step can be graph-captured.  Here the caller
+// hands over one device arena and the library only carves it.
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "pd_internal.h"
+
+struct pd_handle {
+  pd_config cfg;
+  pd_layout lay;
+  char* arena;
+  int device;
+  int num_cus;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBatch = 1024;  // one scan workgroup covers the batch
+constexpr int kMaxSplits = 256;
+constexpr int kMaxGroup = 16;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+pd_status check_config(const pd_config* c) {
+  if (!c) return PD_E_INVALID;
+  if (c->n_layers < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->page_size < 1 ||
+      c->max_batch < 1 || c->max_splits < 1 || c->max_pages_per_req < 1 ||
+      c->num_slots < c->page_size || c->max_total_tokens < 1)
+    return PD_E_INVALID;
+  if (c->head_dim != 64 && c->head_dim != 128) return PD_E_UNSUPPORTED;
+  if (c->n_heads % c->n_kv_heads != 0) return PD_E_UNSUPPORTED;
+  if (c->n_heads / c->n_kv_heads > kMaxGroup) return PD_E_UNSUPPORTED;
+  if (c->max_batch > kMaxBatch || c->max_splits > kMaxSplits) return PD_E_UNSUPPORTED;
+  // Slot ids, token offsets and per-request capacities are int32.
+  if (c->num_slots > INT32_MAX || c->max_total_tokens > INT32_MAX ||
+      (int64_t)c->max_pages_per_req * c->page_size > INT32_MAX)
+    return PD_E_UNSUPPORTED;
+  return PD_OK;
+}
+
+pd_layout make_layout(const pd_config* c) {
+  pd_layout l;
+  memset(&l, 0, sizeof(l));
+  size_t off = 0;
+  l.kv_indptr = off;
+  off = align_up(off + (size_t)(c->max_batch + 1) * 4);
+  l.kv_indices = off;
+  off = align_up(off + (size_t)c->max_total_tokens * 4);
+  const size_t rows = (size_t)c->max_batch * c->n_heads * c->max_splits;
+  l.o_part = off;
+  off = align_up(off + rows * c->head_dim * 4);
+  l.ml_part = off;
+  off = align_up(off + rows * 2 * 4);
+  l.meta = off;
+  off = align_up(off + 16 * 4);
+  l.error_word = off;
+  off = align_up(off + 4);
+  l.arena_bytes = off;
+  return l;
+}
+
+template <typename T>
+T* at(const pd_handle* h, size_t off) {
+  return reinterpret_cast<T*>(h->arena + off);
+}
+
+pd_status hip_status(hipError_t e) { return e == hipSuccess ? PD_OK : PD_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+pd_status paged_decode_workspace_bytes(const pd_config* cfg, size_t* bytes) {
+  if (!bytes) return PD_E_INVALID;
+  pd_status s = check_config(cfg);
+  if (s != PD_OK) return s;
+  *bytes = make_layout(cfg).arena_bytes;
+  return PD_OK;
+}
+
+pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena, size_t arena_bytes,
+                                      pd_handle** out) {
+  if (!out) return PD_E_INVALID;
+  *out = nullptr;
+  pd_status s = check_config(cfg);
+  if (s != PD_OK) return s;
+  if (!d_arena || !aligned(d_arena, kAlign)) return PD_E_INVALID;
+  pd_layout lay = make_layout(cfg);
+  if (arena_bytes < lay.arena_bytes) return PD_E_CAPACITY;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PD_E_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return PD_E_HIP;
+  pd_handle* h = new (std::nothrow) pd_handle;
+  if (!h) return PD_E_CAPACITY;
+  h->cfg = *cfg;
+  h->lay = lay;
+  h->arena = static_cast<char*>(d_arena);
+  h->device = dev;
+  h->num_cus = cus > 0 ? cus : 256;
+  // Start from an empty step: zero kv_indptr, meta and the error word so an
+  // attention call before the first bind sees no tokens.
+  hipError_t e = hipMemsetAsync(h->arena + lay.kv_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
+  if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.meta, 0, 16 * 4, nullptr);
+  if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.error_word, 0, 4, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    delete h;
+    return PD_E_HIP;
+  }
+  *out = h;
+  return PD_OK;
+}
+
+pd_status paged_decode_layout(const pd_handle* h, pd_layout* out) {
+  if (!h || !out) return PD_E_INVALID;
+  *out = h->lay;
+  return PD_OK;
+}
+
+pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t requested,
+                                  int32_t* num_splits) {
+  if (!h || !num_splits || batch < 1 || requested < 0) return PD_E_INVALID;
+  if (batch > h->cfg.max_batch) return PD_E_CAPACITY;
+  if (requested > 0) {
+    if (requested > h->cfg.max_splits) return PD_E_CAPACITY;
+    *num_splits = requested;
+    return PD_OK;
+  }
+  // About eight 4-wave workgroups per compute unit over batch x kv heads, but
+  // no finer than 4 pages per split for a full-length request.
+  const int64_t target = 8LL * h->num_cus;
+  const int64_t per = (int64_t)batch * h->cfg.n_kv_heads;
+  int64_t S = (target + per - 1) / per;
+  int64_t by_len = h->cfg.max_pages_per_req / 4;
+  if (by_len < 1) by_len = 1;
+  if (S > by_len) S = by_len;
+  if (S > h->cfg.max_splits) S = h->cfg.max_splits;
+  if (S < 1) S = 1;
+  *num_splits = (int32_t)S;
+  return PD_OK;
+}
+
+pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
+                            int32_t* d_position_ids, const int32_t* d_req_to_page,
+                            hipStream_t stream) {
+  if (!h || !d_seq_lens || !d_req_to_page || batch < 1) return PD_E_INVALID;
+  if (mode != PD_BIND_FULL && mode != PD_BIND_STEADY) return PD_E_INVALID;
+  if (mode == PD_BIND_STEADY && !d_position_ids) return PD_E_INVALID;
+  if (!aligned(d_seq_lens, 4) || !aligned(d_req_to_page, 4) ||
+      (d_position_ids && !aligned(d_position_ids, 4)))
+    return PD_E_INVALID;
+  if (batch > h->cfg.max_batch) return PD_E_CAPACITY;
+  pd::BindArgs a;
+  a.batch = batch;
+  a.mode = mode;
+  a.page_size = h->cfg.page_size;
+  a.max_pages_per_req = h->cfg.max_pages_per_req;
+  a.num_pages = h->cfg.num_slots / h->cfg.page_size;
+  a.max_total_tokens = h->cfg.max_total_tokens;
+  a.seq_lens = d_seq_lens;
+  a.position_ids = d_position_ids;
+  a.req_to_page = d_req_to_page;
+  a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
+  a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
+  a.meta = at<int32_t>(h, h->lay.meta);
+  a.error_word = at<uint32_t>(h, h->lay.error_word);
+  return hip_status(pd::launch_bind(a, stream));
+}
+
+pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
+                            const void* d_q, const void* d_k_store, const void* d_v_store,
+                            float scale, hipStream_t stream) {
+  if (!h || !d_q || !d_k_store || !d_v_store || batch < 1 || num_splits < 1 || layer < 0)
+    return PD_E_INVALID;
+  if (!aligned(d_q, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16))
+    return PD_E_INVALID;
+  const pd_config& c = h->cfg;
+  if (batch > c.max_batch || num_splits > c.max_splits || layer >= c.n_layers)
+    return PD_E_CAPACITY;
+  const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
+  pd::AttnArgs a;
+  a.batch = batch;
+  a.n_heads = c.n_heads;
+  a.n_kv_heads = c.n_kv_heads;
+  a.group = c.n_heads / c.n_kv_heads;
+  a.page_size = c.page_size;
+  a.num_splits = num_splits;
+  a.max_splits = c.max_splits;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.q = static_cast<const uint16_t*>(d_q);
+  a.k_layer = static_cast<const uint16_t*>(d_k_store) + (int64_t)layer * layer_elems;
+  a.v_layer = static_cast<const uint16_t*>(d_v_store) + (int64_t)layer * layer_elems;
+  a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
+  a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
+  a.meta = at<int32_t>(h, h->lay.meta);
+  a.o_part = at<float>(h, h->lay.o_part);
+  a.ml_part = at<float>(h, h->lay.ml_part);
+  return hip_status(pd::launch_attn(a, c.head_dim, stream));
+}
+
+pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
+                             hipStream_t stream) {
+  if (!h || !d_out || batch < 1 || num_splits < 1) return PD_E_INVALID;
+  if (!aligned(d_out, 16)) return PD_E_INVALID;
+  if (batch > h->cfg.max_batch || num_splits > h->cfg.max_splits) return PD_E_CAPACITY;
+  pd::MergeArgs a;
+  a.batch = batch;
+  a.n_heads = h->cfg.n_heads;
+  a.num_splits = num_splits;
+  a.max_splits = h->cfg.max_splits;
+  a.o_part = at<float>(h, h->lay.o_part);
+  a.ml_part = at<float>(h, h->lay.ml_part);
+  a.out = static_cast<uint16_t*>(d_out);
+  return hip_status(pd::launch_merge(a, h->cfg.head_dim, stream));
+}
+
+pd_status paged_decode_read_error(pd_handle* h, uint32_t* flags, hipStream_t stream) {
+  if (!h || !flags) return PD_E_INVALID;
+  uint32_t v = 0;
+  void* w = h->arena + h->lay.error_word;
+  hipError_t e = hipMemcpyAsync(&v, w, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemsetAsync(w, 0, 4, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return PD_E_HIP;
+  *flags = v;
+  return PD_OK;
+}
+
+pd_status paged_decode_destroy(pd_handle* h) {
+  if (!h) return PD_E_INVALID;
+  delete h;
+  return PD_OK;
+}
+
+const char* paged_decode_strerror(int status) {
+  switch (status) {
+    case PD_OK: return "ok";
+    case PD_E_INVALID: return "invalid argument (null or misaligned pointer, bad dimension or mode)";
+    case PD_E_UNSUPPORTED: return "unsupported configuration (head_dim, head grouping or limits)";
+    case PD_E_CAPACITY: return "capacity exceeded (batch, splits, layer or arena size)";
+    case PD_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal declarations shared by the host ABI and the kernel translation
+// units of libpaged_decode.so.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/paged_decode.h"
+
+namespace pd {
+
+// Words of the arena's meta block written by the bind scan.
+enum MetaWord : int {
+  kMetaMaxPages = 0,     // max over requests of ceil(L_b / page_size)
+  kMetaTotalTokens = 1,  // sum of the (clamped) lengths
+};
+
+struct BindArgs {
+  int32_t batch;
+  int32_t mode;
+  int32_t page_size;
+  int32_t max_pages_per_req;
+  int64_t num_pages;          // num_slots / page_size
+  int64_t max_total_tokens;
+  int32_t* seq_lens;
+  int32_t* position_ids;      // may be null
+  const int32_t* req_to_page;
+  int32_t* kv_indptr;
+  int32_t* kv_indices;
+  int32_t* meta;
+  uint32_t* error_word;
+};
+
+struct AttnArgs {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t group;              // n_heads / n_kv_heads
+  int32_t page_size;
+  int32_t num_splits;         // S used for this launch
+  int32_t max_splits;         // stride of the partial buffers
+  float scale_log2;           // scale * log2(e)
+  const uint16_t* q;          // bf16 [batch, n_heads, D]
+  const uint16_t* k_layer;    // bf16 [num_slots, n_kv_heads, D] of this layer
+  const uint16_t* v_layer;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* meta;
+  float* o_part;              // [max_batch, n_heads, max_splits, D]
+  float* ml_part;             // [max_batch, n_heads, max_splits, 2]
+};
+
+struct MergeArgs {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t num_splits;
+  int32_t max_splits;
+  const float* o_part;
+  const float* ml_part;
+  uint16_t* out;              // bf16 [batch, n_heads, D]
+};
+
+hipError_t launch_bind(const BindArgs& a, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace pd

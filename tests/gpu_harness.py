@@ -1,0 +1,123 @@
+"""Shared helpers for the GPU tests: device copies, the workspace for a
+workload, and comparisons against the CPU oracle at the stated tolerances.
+
+Tolerances (bf16 inputs, fp32 accumulation):
+  decode_out and o_part:  |x - ref| <= 1e-2 + 1e-2 * |ref|   elementwise
+  per-split lse:          |lse - ref| <= 1e-4 * max(1, |ref|); empty splits
+                          must be exactly -inf
+  kv_indptr, kv_indices:  bit-exact
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_decode_10_amd import Config, PagedDecode
+
+OUT_ATOL = 1e-2
+OUT_RTOL = 1e-2
+LSE_RTOL = 1e-4
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@dataclass
+class Dev:
+    seq_lens: torch.Tensor
+    position_ids: torch.Tensor
+    req_to_page: torch.Tensor
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+
+
+def to_device(w) -> Dev:
+    return Dev(w.seq_lens.cuda(), w.position_ids.cuda(), w.req_to_page.cuda().contiguous(),
+               w.q.cuda(), w.k_store.cuda(), w.v_store.cuda())
+
+
+def make_ws(w, max_splits=64, extra_tokens=None) -> PagedDecode:
+    if extra_tokens is None:
+        extra_tokens = w.meta.get("growth", 0) * w.batch
+    cfg = Config(n_layers=w.n_layers, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                 page_size=w.page_size, max_batch=w.batch, max_splits=max_splits,
+                 max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
+                 max_total_tokens=max(1, int(w.seq_lens.sum()) + extra_tokens))
+    return PagedDecode(cfg)
+
+
+def check_bind(ws, w, seq_lens_host):
+    B = w.batch
+    ip, ix = oracle.bind_full(seq_lens_host, w.req_to_page.numpy(), w.page_size)
+    got_ip = ws.kv_indptr[: B + 1].cpu().numpy()
+    assert np.array_equal(got_ip, ip), (got_ip, ip)
+    got_ix = ws.kv_indices[: int(ip[-1])].cpu().numpy()
+    assert np.array_equal(got_ix, ix), "kv_indices differ"
+    return ip, ix
+
+
+def assert_close_out(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ok = np.abs(got - ref) <= OUT_ATOL + OUT_RTOL * np.abs(ref)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance; first "
+                             f"{[(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in bad]}")
+
+
+def assert_close_lse(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), empty), f"{what}: empty-split pattern differs"
+    g, r = got[~empty], ref[~empty]
+    ok = np.abs(g - r) <= LSE_RTOL * np.maximum(1.0, np.abs(r))
+    if not ok.all():
+        i = int(np.argmax(~ok))
+        raise AssertionError(f"{what}: {int((~ok).sum())} lse values off, e.g. {g[i]} vs {r[i]}")
+
+
+def run_layer(ws, w, dev, layer, S, out=None):
+    B = w.batch
+    if out is None:
+        out = torch.empty((B, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws.attn(B, layer, S, dev.q[layer], dev.k, dev.v, w.scale)
+    ws.merge(B, S, out)
+    return out
+
+
+def check_layer(ws, w, dev, layer, S, seq_lens_host=None, pairs=None, parts=True, out=None):
+    """Run attn+merge for one layer and compare with the oracle."""
+    B, H = w.batch, w.n_heads
+    L = w.seq_lens.numpy() if seq_lens_host is None else np.asarray(seq_lens_host)
+    out = run_layer(ws, w, dev, layer, S, out)
+    torch.cuda.synchronize()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    ref, ref_lse = oracle.decode_attention(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix,
+                                           w.scale, w.n_kv_heads, pairs=pairs)
+    G = w.group
+    heads = [(b, h) for b, g in (pairs or [(b, g) for b in range(B) for g in range(w.n_kv_heads)])
+             for h in range(g * G, (g + 1) * G)]
+    got = out.float().cpu().numpy()
+    bi = np.array([x[0] for x in heads])
+    hi = np.array([x[1] for x in heads])
+    assert np.isfinite(got[bi, hi]).all(), "non-finite output"
+    assert_close_out(got[bi, hi], ref[bi, hi], f"decode_out layer {layer} S={S}")
+    if parts:
+        o, m, lse = oracle.split_partials(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix,
+                                          w.scale, w.n_kv_heads, w.page_size, S, pairs=pairs)
+        op = ws.o_part[:B, :, :S].cpu().numpy()
+        mlp = ws.ml_part[:B, :, :S].cpu().numpy()
+        assert_close_out(op[bi, hi], o[bi, hi], f"o_part layer {layer} S={S}")
+        lse_gpu = np.where(np.isneginf(mlp[..., 0]), -np.inf, mlp[..., 0].astype(np.float64) + mlp[..., 1])
+        assert_close_lse(lse_gpu[bi, hi], lse[bi, hi], f"lse layer {layer} S={S}")
+        # the max itself (natural units) is the split's max scaled score
+        mm = m[bi, hi]
+        fin = np.isfinite(mm)
+        assert np.all(np.abs(mlp[bi, hi][..., 0][fin] - mm[fin]) <= 1e-4 * np.maximum(1, np.abs(mm[fin])))
+    return out, ref

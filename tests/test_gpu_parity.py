@@ -1,0 +1,406 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test builds seeded inputs with ``workloads``, runs bind / attn / merge
+in the library's kernels and compares with ``oracle`` on the same inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from paged_kv_decode_10_amd import (PD_BIND_FULL, PD_BIND_STEADY, PD_ERR_BAD_PAGE, PD_ERR_NEG_SEQ_LEN,
+                                    PD_ERR_SEQ_OVER_TABLE, PD_ERR_TOTAL_OVER_CAP, PagedDecodeError)
+from tests.gpu_harness import check_bind, check_layer, make_ws, run_layer, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+
+
+def _bind(ws, w, dev, mode=PD_BIND_FULL):
+    ws.bind(w.batch, mode, dev.seq_lens, dev.position_ids, dev.req_to_page)
+
+
+# ------------------------------------------------------------------ tiny ----
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 7, 16])
+def test_tiny_parity(S):
+    say(f"[tiny] S={S}")
+    w = workloads.make("tiny")
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    torch.cuda.synchronize()
+    check_bind(ws, w, w.seq_lens.numpy())
+    check_layer(ws, w, dev, 0, S)
+    assert ws.read_error() == 0
+
+
+def test_tiny_auto_splits():
+    w = workloads.make("tiny")
+    dev = to_device(w)
+    ws = make_ws(w)
+    S = ws.num_splits(w.batch)
+    say(f"[tiny] auto S={S}")
+    assert 1 <= S <= 64
+    _bind(ws, w, dev)
+    check_layer(ws, w, dev, 0, S)
+
+
+# --------------------------------------------------- shapes and groupings ----
+
+@pytest.mark.parametrize("G,hkv,D,ps", [(1, 4, 128, 16), (2, 2, 64, 16), (3, 2, 128, 16), (4, 8, 128, 16),
+                                        (5, 2, 64, 8), (8, 8, 128, 16), (8, 1, 64, 32), (16, 2, 128, 16),
+                                        (4, 2, 128, 1), (4, 2, 64, 7)])
+@pytest.mark.parametrize("S", [1, 5])
+def test_grouping_and_page_sizes(G, hkv, D, ps, S):
+    say(f"[shape] G={G} hkv={hkv} D={D} ps={ps} S={S}")
+    w = workloads.make_custom("shape", seed=100 + G * 7 + D + ps, n_layers=2, seq_lens=[1, 33, 250, 17],
+                              n_heads=G * hkv, n_kv_heads=hkv, head_dim=D, page_size=ps)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    torch.cuda.synchronize()
+    check_bind(ws, w, w.seq_lens.numpy())
+    check_layer(ws, w, dev, 1, S)
+
+
+def test_empty_request_and_more_splits_than_pages():
+    say("[edge] empty request, S > pages")
+    w = workloads.make_custom("edge", seed=7, n_layers=1, seq_lens=[0, 20, 3, 0], n_heads=8, n_kv_heads=2,
+                              head_dim=128, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    out, _ = check_layer(ws, w, dev, 0, 9)
+    got = out.float().cpu()
+    assert torch.all(got[0] == 0) and torch.all(got[3] == 0)
+    ml = ws.ml_part[:4, :, :9].cpu()
+    assert torch.all(torch.isneginf(ml[0])) and torch.all(torch.isneginf(ml[3]))
+
+
+def test_all_requests_empty():
+    say("[edge] all empty")
+    w = workloads.make_custom("edge0", seed=8, n_layers=1, seq_lens=[0, 0], n_heads=4, n_kv_heads=1,
+                              head_dim=64, page_size=16, num_pages=4)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    out = run_layer(ws, w, dev, 0, 3)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0)
+    assert ws.kv_indptr[:3].cpu().tolist() == [0, 0, 0]
+
+
+# ------------------------------------------------------------ closed forms ----
+
+def test_single_token_is_value_row_bit_exact():
+    """L = 1: the weight is 1 and the output is the V row itself."""
+    say("[closed] L=1")
+    w = workloads.make_custom("one", seed=9, n_layers=1, seq_lens=[1, 1, 1], n_heads=16, n_kv_heads=4,
+                              head_dim=128, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    for S in (1, 4):
+        out = run_layer(ws, w, dev, 0, S)
+        torch.cuda.synchronize()
+        for b in range(3):
+            slot = int(w.req_to_page[b, 0]) * w.page_size
+            vrow = w.v_store[0, slot]  # [Hkv, D]
+            want = vrow.repeat_interleave(w.group, dim=0)
+            assert torch.equal(out[b].cpu().view(torch.int16), want.view(torch.int16))
+
+
+def test_constant_keys_give_mean_of_values():
+    say("[closed] constant keys")
+    w = workloads.make_custom("constk", seed=10, n_layers=1, seq_lens=[300, 77], n_heads=8, n_kv_heads=2,
+                              head_dim=64, page_size=16)
+    ip, ix = oracle.bind_full(w.seq_lens.numpy(), w.req_to_page.numpy(), w.page_size)
+    w.k_store[0, torch.from_numpy(ix)] = w.k_store[0, int(ix[0])].clone()
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    out = run_layer(ws, w, dev, 0, 4)
+    torch.cuda.synchronize()
+    for b in range(2):
+        rows = w.v_store[0, torch.from_numpy(ix[ip[b]:ip[b + 1]])].double()  # [L, Hkv, D]
+        mean = rows.mean(0).repeat_interleave(w.group, 0)
+        err = (out[b].double().cpu() - mean).abs()
+        assert torch.all(err <= 1e-2 + 1e-2 * mean.abs())
+
+
+def test_large_scores_no_overflow():
+    """q scaled x40: scores far above exp's range unless shifted by the max."""
+    say("[closed] large scores")
+    w = workloads.make_custom("big", seed=11, n_layers=1, seq_lens=[500, 64], n_heads=8, n_kv_heads=2,
+                              head_dim=128, page_size=16, q_scale=40.0)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    check_layer(ws, w, dev, 0, 3)
+
+
+# ------------------------------------------------------------ invariances ----
+
+def test_page_permutation_bit_identical():
+    say("[inv] page permutation")
+    w = workloads.make("tiny")
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    out1 = run_layer(ws, w, dev, 0, 4).clone()
+    # move every assigned page to another free-or-used page, same logical cache
+    ip, ix = oracle.bind_full(w.seq_lens.numpy(), w.req_to_page.numpy(), w.page_size)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(w.num_pages)
+    t2 = w.req_to_page.clone()
+    used = t2 >= 0
+    t2[used] = torch.from_numpy(perm[: int(used.sum())]).to(torch.int32)
+    ix2 = oracle.kv_indices(w.seq_lens.numpy(), t2.numpy(), w.page_size)
+    k2 = torch.full_like(w.k_store, float("nan"))
+    v2 = torch.full_like(w.v_store, float("nan"))
+    k2[0, torch.from_numpy(ix2)] = w.k_store[0, torch.from_numpy(ix)]
+    v2[0, torch.from_numpy(ix2)] = w.v_store[0, torch.from_numpy(ix)]
+    dev.k, dev.v, dev.req_to_page = k2.cuda(), v2.cuda(), t2.cuda()
+    _bind(ws, w, dev)
+    out2 = run_layer(ws, w, dev, 0, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_split_count_consistency_and_determinism():
+    say("[inv] split count / determinism")
+    w = workloads.make_custom("inv", seed=12, n_layers=1, seq_lens=[1000, 3000, 17], n_heads=32,
+                              n_kv_heads=8, head_dim=128, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    outs = {}
+    for S in (1, 2, 8, 32, 64):
+        outs[S] = run_layer(ws, w, dev, 0, S).clone()
+        again = run_layer(ws, w, dev, 0, S)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[S].view(torch.int16), again.view(torch.int16)), "not deterministic"
+    for S in (2, 8, 32, 64):
+        d = (outs[S].double() - outs[1].double()).abs()
+        assert torch.all(d <= 2e-2 + 2e-2 * outs[1].double().abs()).item()
+
+
+# --------------------------------------------------------- larger configs ----
+
+def test_b1_parity():
+    say("[b1] B=1 L=4096 H=32 Hkv=8 D=128")
+    w = workloads.make("b1")
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    torch.cuda.synchronize()
+    check_bind(ws, w, w.seq_lens.numpy())
+    S = ws.num_splits(1)
+    say(f"[b1] auto S={S}")
+    check_layer(ws, w, dev, 0, S)
+    check_layer(ws, w, dev, 0, 32, parts=False)
+
+
+def test_b16_ragged_parity():
+    say("[b16] B=16 L~U[512,8192]")
+    w = workloads.make("b16")
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    torch.cuda.synchronize()
+    check_bind(ws, w, w.seq_lens.numpy())
+    S = ws.num_splits(w.batch)
+    say(f"[b16] auto S={S}")
+    check_layer(ws, w, dev, 0, S)
+
+
+def test_long_context_sampled():
+    say("[long] B=4 L=131072 H=64 Hkv=8")
+    w = workloads.make("long")
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    torch.cuda.synchronize()
+    check_bind(ws, w, w.seq_lens.numpy())
+    S = ws.num_splits(w.batch)
+    say(f"[long] auto S={S}")
+    assert S >= 32
+    pairs = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    check_layer(ws, w, dev, 0, S, pairs=pairs)
+    check_layer(ws, w, dev, 0, 32, pairs=[(3, 2)])
+    assert ws.read_error() == 0
+
+
+# ------------------------------------------------- steady bind and graphs ----
+
+def test_steady_bind_updates_in_place():
+    say("[bind] steady")
+    w = workloads.make_custom("steady", seed=13, n_layers=2, seq_lens=[5, 16, 31, 100], n_heads=8,
+                              n_kv_heads=2, head_dim=64, page_size=16, growth=40)
+    dev = to_device(w)
+    ws = make_ws(w)
+    _bind(ws, w, dev)
+    L = w.seq_lens.numpy().astype(np.int64)
+    pos = w.position_ids.numpy().astype(np.int64)
+    for step in range(3):
+        _bind(ws, w, dev, PD_BIND_STEADY)
+        L, pos = oracle.bind_steady(L, pos)
+        torch.cuda.synchronize()
+        assert dev.seq_lens.cpu().tolist() == L.tolist()
+        assert dev.position_ids.cpu().tolist() == pos.tolist()
+        check_bind(ws, w, L)
+    check_layer(ws, w, dev, 1, 3, seq_lens_host=L)
+
+
+def test_graph_replay_bit_identical_and_allocation_free():
+    """[bind steady, n_layers x (attn, merge)] captured once and replayed."""
+    say("[graph] capture + replay")
+    w = workloads.make_custom("gstep", seed=14, n_layers=4, seq_lens=lambda g: torch.randint(1, 300, (8,), generator=g).tolist(),
+                              n_heads=32, n_kv_heads=8, head_dim=128, page_size=16, growth=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    B = w.batch
+    S = ws.num_splits(B)
+    out = torch.empty((w.n_layers, B, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    sl0, pos0 = dev.seq_lens.clone(), dev.position_ids.clone()
+
+    def step():
+        ws.bind(B, PD_BIND_STEADY, dev.seq_lens, dev.position_ids, dev.req_to_page)
+        for layer in range(w.n_layers):
+            ws.attn(B, layer, S, dev.q[layer], dev.k, dev.v, w.scale)
+            ws.merge(B, S, out[layer])
+
+    # eager reference: 5 steps
+    _bind(ws, w, dev)
+    eager = []
+    for _ in range(5):
+        step()
+        eager.append(out.clone())
+    torch.cuda.synchronize()
+    # graph: reset state, live run first, then capture
+    dev.seq_lens.copy_(sl0)
+    dev.position_ids.copy_(pos0)
+    _bind(ws, w, dev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    assert dev.seq_lens.cpu().tolist() == sl0.cpu().tolist(), "capture must not execute"
+    for i in range(5):
+        a0 = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+        g.replay()
+        torch.cuda.synchronize()
+        a1 = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+        assert a1 == a0, "replay allocated device memory"
+        assert torch.equal(out.view(torch.int16), eager[i].view(torch.int16)), f"replay {i} differs"
+        _ = (out.float().sum()).item()  # eager work between replays
+    assert dev.seq_lens.cpu().tolist() == (sl0 + 5).cpu().tolist()
+    # parity of the last replay against the oracle
+    L = (sl0 + 5).cpu().numpy()
+    check_layer(ws, w, dev, 3, S, seq_lens_host=L)
+
+
+def test_full_step_config_sampled():
+    """24-layer step: steady bind + 24 x (attn, merge), graph-replayed, sampled parity."""
+    say("[step] 24 layers B=32 L~U[1,2048] graph")
+    w = workloads.make("step")
+    dev = to_device(w)
+    ws = make_ws(w)
+    B = w.batch
+    S = ws.num_splits(B)
+    say(f"[step] S={S}")
+    out = torch.empty((w.n_layers, B, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        ws.bind(B, PD_BIND_STEADY, dev.seq_lens, dev.position_ids, dev.req_to_page)
+        for layer in range(w.n_layers):
+            ws.attn(B, layer, S, dev.q[layer], dev.k, dev.v, w.scale)
+            ws.merge(B, S, out[layer])
+
+    _bind(ws, w, dev)
+    step()  # live run before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    L = dev.seq_lens.cpu().numpy()
+    assert L.tolist() == (w.seq_lens.numpy() + 4).tolist()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    pairs = [(0, 0), (7, 3), (19, 7), (31, 5)]
+    got = out.float().cpu().numpy()
+    for layer in (0, 11, 23):
+        ref, _ = oracle.decode_attention(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix,
+                                         w.scale, w.n_kv_heads, pairs=pairs)
+        for b, gk in pairs:
+            hs = slice(gk * w.group, (gk + 1) * w.group)
+            r = ref[b, hs]
+            assert np.all(np.abs(got[layer, b, hs] - r) <= 1e-2 + 1e-2 * np.abs(r)), (layer, b, gk)
+    assert ws.read_error() == 0
+
+
+# ------------------------------------------------------------- error paths ----
+
+def test_device_error_word_and_clamping():
+    say("[err] device error word")
+    w = workloads.make_custom("err", seed=15, n_layers=1, seq_lens=[20, 40], n_heads=4, n_kv_heads=2,
+                              head_dim=64, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    assert ws.read_error() == 0
+    cap = w.max_pages_per_req * w.page_size
+    dev.seq_lens.copy_(torch.tensor([cap + 5, -3], dtype=torch.int32))
+    _bind(ws, w, dev)
+    flags = ws.read_error()
+    assert flags & PD_ERR_SEQ_OVER_TABLE and flags & PD_ERR_NEG_SEQ_LEN
+    assert ws.kv_indptr[:3].cpu().tolist() == [0, cap, cap]
+    assert ws.read_error() == 0  # cleared
+    # a bad page id inside the length
+    dev.seq_lens.copy_(w.seq_lens.cuda())
+    t = w.req_to_page.clone()
+    t[1, 0] = w.num_pages + 3
+    dev.req_to_page = t.cuda()
+    _bind(ws, w, dev)
+    assert ws.read_error() & PD_ERR_BAD_PAGE
+    # total over kv_indices capacity
+    ws2 = make_ws(w, extra_tokens=-30)
+    dev.req_to_page = w.req_to_page.cuda()
+    ws2.bind(w.batch, PD_BIND_FULL, dev.seq_lens, dev.position_ids, dev.req_to_page)
+    assert ws2.read_error() & PD_ERR_TOTAL_OVER_CAP
+    ip = ws2.kv_indptr[:3].cpu().tolist()
+    assert ip[-1] == int(w.seq_lens.sum()) - 30
+    run_layer(ws2, w, dev, 0, 2)  # clipped lengths: runs in bounds
+    torch.cuda.synchronize()
+
+
+def test_host_side_errors():
+    say("[err] host-side status codes")
+    w = workloads.make("tiny")
+    dev = to_device(w)
+    ws = make_ws(w, max_splits=8)
+    with pytest.raises(PagedDecodeError):
+        ws.attn(w.batch, 0, 9, dev.q[0], dev.k, dev.v, w.scale)  # S > max_splits
+    q_big = torch.zeros((w.batch + 1, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(PagedDecodeError):
+        ws.attn(w.batch + 1, 0, 1, q_big, dev.k, dev.v, w.scale)  # batch > max_batch
+    with pytest.raises(ValueError):
+        ws.attn(w.batch, 0, 1, dev.q[0][:1], dev.k, dev.v, w.scale)  # q too small: caught in Python
+    with pytest.raises(PagedDecodeError):
+        ws.attn(w.batch, 1, 1, dev.q[0], dev.k, dev.v, w.scale)  # layer out of range
+    with pytest.raises(PagedDecodeError):
+        ws.bind(w.batch, 5, dev.seq_lens, dev.position_ids, dev.req_to_page)  # bad mode
+    with pytest.raises(PagedDecodeError):
+        ws.num_splits(w.batch, 9)
+    assert math.isfinite(w.scale)
