@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark: split-KV paged decode attention on one MI355X.
+
+One step = the whole decode hot path for one batch: steady bind (seq_lens and
+position_ids +1, kv_indptr scan, kv_indices fill) followed by 24 layers of
+(split-KV attention, log-sum-exp merge), captured once into a hipGraph and
+replayed.  Workload: 24 layers in [24, slots, 8, 128] bf16 stores, B=32,
+seq_lens ~ U[1, 2048] (+1 per step), 32 query heads, page size 16.
+
+Prints ONE JSON line on stdout.  ``value`` is KV bytes read per second (K and
+V rows actually attended, summed over layers and steps) over the timed graph
+replays.  ``roofline`` is for the dominant kernel (the split attention),
+timed live with HIP events on its stream over a replayed graph of the 24
+attention launches.  ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the same workload.  Diagnostics go to stderr.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV HBM GB/s (% of peak) and µs/layer at B=1..32"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+ATTN_SOURCES = ("paged_kv_decode_10_amd/csrc/attn_mfma.hip", "paged_kv_decode_10_amd/csrc/attn_kernels.hip",
+                "paged_kv_decode_10_amd/csrc/pd_internal.h", "paged_kv_decode_10_amd/csrc/paged_decode.cpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_kernel_digest() -> str:
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_bytes(seq_lens, n_kv_heads, head_dim, batch, n_heads, num_splits):
+    """Algorithmic bytes of one attention launch: K+V rows, kv_indices, q, partial writes."""
+    tok = int(seq_lens.sum())
+    kv = tok * n_kv_heads * head_dim * 2 * 2
+    idx = tok * 4
+    q = batch * n_heads * head_dim * 2
+    parts = batch * n_heads * num_splits * (head_dim * 4 + 8)
+    return kv, kv + idx + q + parts
+
+
+def cpu_baseline(w, budget_s: float, num_splits: int):
+    """Time the oracle on the same step, layer after layer, until ~budget_s.
+
+    Per layer it computes what the GPU path produces: the bind (kv_indptr,
+    kv_indices), the per-split partials and the merged attention output.
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    L = w.seq_lens.numpy()
+    layers, kv = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        layer = layers % w.n_layers
+        ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+        oracle.split_partials(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix, w.scale,
+                              w.n_kv_heads, w.page_size, num_splits)
+        oracle.decode_attention(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix, w.scale,
+                                w.n_kv_heads)
+        layers += 1
+        kv += int(L.sum()) * w.n_kv_heads * w.head_dim * 2 * 2
+    dt = time.perf_counter() - t0
+    cores = max(torch.get_num_threads(), blas)
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 numpy oracle on the same decode step: {layers} layer passes (bind, "
+                      f"per-split partials with S={num_splits}, merged attention; all 32 requests x 8 kv "
+                      f"heads), {kv / 1e6:.0f} MB of KV in {dt:.1f} s; host affinity "
+                      f"{len(os.sched_getaffinity(0))} cpus, torch threads {torch.get_num_threads()}, "
+                      f"BLAS threads {blas}; numpy {np.__version__}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see the sharding note in DESIGN.md).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+    from paged_kv_decode_10_amd import PD_BIND_FULL, PD_BIND_STEADY, Config, PagedDecode
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 2
+    K, W = args.steps, args.warmup
+    growth = max(256, K + W + 8)
+    t0 = time.perf_counter()
+    w = workloads.make("step", growth=growth)
+    log(f"[bench] workload generated in {time.perf_counter() - t0:.1f}s: B={w.batch} layers={w.n_layers} "
+        f"sum(L)={int(w.seq_lens.sum())} pages={w.num_pages}")
+    B, H, Hkv, D, NL = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.n_layers
+    cfg = Config(n_layers=NL, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size, max_batch=B,
+                 max_splits=64, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
+                 max_total_tokens=int(w.seq_lens.sum()) + growth * B)
+    ws = PagedDecode(cfg)
+    seq = w.seq_lens.cuda()
+    pos = w.position_ids.cuda()
+    table = w.req_to_page.cuda()
+    q = w.q.cuda()
+    kst = w.k_store.cuda()
+    vst = w.v_store.cuda()
+    out = torch.empty((NL, B, H, D), dtype=torch.bfloat16, device="cuda")
+    S = ws.num_splits(B, args.splits)
+    log(f"[bench] splits S={S}")
+
+    def step():
+        ws.bind(B, PD_BIND_STEADY, seq, pos, table)
+        for layer in range(NL):
+            ws.attn(B, layer, S, q[layer], kst, vst, w.scale)
+            ws.merge(B, S, out[layer])
+
+    L0 = w.seq_lens.to(torch.int64)
+    ws.bind(B, PD_BIND_FULL, seq, pos, table)
+    step()  # live run before capture
+    torch.cuda.synchronize()
+    done = 1
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(W):
+        graph.replay()
+    torch.cuda.synchronize()
+    done += W
+    assert ws.read_error() == 0, "device error word set"
+
+    kv_bytes = 0
+    for i in range(K):
+        kv_bytes += int((L0 + done + i + 1).sum()) * Hkv * D * 4 * NL
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    done += K
+    assert torch.equal(seq.cpu().to(torch.int64), L0 + done), "steady bind did not advance once per step"
+    gbs = kv_bytes / (ms / 1e3) / 1e9
+    ms_step = ms / K
+    log(f"[bench] {K} steps in {ms:.2f} ms: {ms_step * 1e3:.1f} us/step, {ms_step * 1e3 / NL:.2f} us/layer, "
+        f"{gbs:.0f} GB/s KV ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+
+    # Roofline of the dominant kernel: a graph of the 24 attention launches at
+    # the current lengths, replayed; HIP events on the launch stream.
+    ag = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ag):
+        for layer in range(NL):
+            ws.attn(B, layer, S, q[layer], kst, vst, w.scale)
+    for _ in range(3):
+        ag.replay()
+    torch.cuda.synchronize()
+    R = args.roofline_reps
+    e0.record()
+    for _ in range(R):
+        ag.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    attn_us = e0.elapsed_time(e1) * 1e3 / (R * NL)
+    Lnow = seq.cpu().to(torch.int64)
+    kv_l, alg_l = attn_bytes(Lnow, Hkv, D, B, H, S)
+    achieved = alg_l / (attn_us * 1e-6) / 1e9
+    log(f"[bench] attention kernel: {attn_us:.2f} us/launch, {alg_l / 1e6:.1f} MB algorithmic "
+        f"({kv_l / 1e6:.1f} MB KV) -> {achieved:.0f} GB/s")
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_digest") == attn_kernel_digest() and tr.get("splits") == S:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "split_attn (paged_decode_attn)", "us_per_launch": round(attn_us, 3),
+                "algorithmic_bytes_per_launch": alg_l}
+
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {n} bytes")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_budget, S)
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode step: 24 layers, B=32, seq_lens~U[1,2048] +1/step, 32 q heads, "
+                               "8 kv heads, head_dim 128, page 16; steady bind + 24 x (split attn, merge), "
+                               "hipGraph replay",
+                   "batch": B, "n_layers": NL, "n_heads": H, "n_kv_heads": Hkv, "head_dim": D,
+                   "page_size": w.page_size, "num_splits": S, "parallelism": "single GPU",
+                   "accumulate": "fp32"},
+        "us_per_layer": round(ms_step * 1e3 / NL, 3),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

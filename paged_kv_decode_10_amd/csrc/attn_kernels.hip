@@ -326,7 +326,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_attn_valu(const AttnArgs& a, int head_dim, hipStream_t stream) {
   if (head_dim == 64) return launch_d<64>(a, stream);
   return launch_d<128>(a, stream);
 }

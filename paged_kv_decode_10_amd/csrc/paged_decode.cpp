@@ -77,6 +77,18 @@ pd_status hip_status(hipError_t e) { return e == hipSuccess ? PD_OK : PD_E_HIP; 
 
 }  // namespace
 
+namespace pd {
+// The matrix-core kernel is the default; building with -DPD_ATTN_VALU selects
+// the VALU kernel instead (for comparisons).
+hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream) {
+#ifdef PD_ATTN_VALU
+  return launch_attn_valu(a, head_dim, stream);
+#else
+  return launch_attn_mfma(a, head_dim, stream);
+#endif
+}
+}  // namespace pd
+
 extern "C" {
 
 pd_status paged_decode_workspace_bytes(const pd_config* cfg, size_t* bytes) {

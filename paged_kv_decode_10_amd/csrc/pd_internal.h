@@ -61,6 +61,9 @@ struct MergeArgs {
 };
 
 hipError_t launch_bind(const BindArgs& a, hipStream_t stream);
+// Split attention kernels: VALU (dot2 + DPP) and matrix-core variants.
+hipError_t launch_attn_valu(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_mfma(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 
