@@ -99,18 +99,15 @@ struct Rows {
   uint4 v[CH];
 };
 
-// K and V chunks of one slot (this lane's slice); slot < 0 loads nothing.
+// K and V chunks of one slot (this lane's slice).  Unconditional, so the
+// compiler can count the loads in flight exactly.
 template <int CH, int LPT>
 __device__ __forceinline__ Rows<CH> load_rows(const uint4* kbase, const uint4* vbase,
                                               int64_t stride16, int ls, int32_t slot) {
   Rows<CH> r;
+  const int64_t off = (int64_t)slot * stride16 + ls;
 #pragma unroll
-  for (int k = 0; k < CH; ++k) { r.k[k] = make_uint4(0, 0, 0, 0); r.v[k] = r.k[k]; }
-  if (slot >= 0) {
-    const int64_t off = (int64_t)slot * stride16 + ls;
-#pragma unroll
-    for (int k = 0; k < CH; ++k) { r.k[k] = kbase[off + LPT * k]; r.v[k] = vbase[off + LPT * k]; }
-  }
+  for (int k = 0; k < CH; ++k) { r.k[k] = kbase[off + LPT * k]; r.v[k] = vbase[off + LPT * k]; }
   return r;
 }
 
@@ -147,18 +144,15 @@ split_attn_valu_kernel(AttnArgs a) {
   uint32_t qv[GP][W];
 #pragma unroll
   for (int h = 0; h < GP; ++h) {
-    if (h < a.group) {
-      const uint4* qp = reinterpret_cast<const uint4*>(
-          a.q + ((int64_t)b * a.n_heads + g * a.group + h) * D);
+    const bool real = h < a.group;  // loads stay unconditional; padded heads get zeros
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        a.q + ((int64_t)b * a.n_heads + g * a.group + (real ? h : 0)) * D);
 #pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        uint4 v = qp[ls + LPT * k];
-        qv[h][4 * k + 0] = v.x; qv[h][4 * k + 1] = v.y;
-        qv[h][4 * k + 2] = v.z; qv[h][4 * k + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < W; ++w) qv[h][w] = 0u;
+    for (int k = 0; k < CH; ++k) {
+      uint4 v = qp[ls + LPT * k];
+      if (!real) v = make_uint4(0, 0, 0, 0);
+      qv[h][4 * k + 0] = v.x; qv[h][4 * k + 1] = v.y;
+      qv[h][4 * k + 2] = v.z; qv[h][4 * k + 3] = v.w;
     }
   }
 
@@ -179,9 +173,12 @@ split_attn_valu_kernel(AttnArgs a) {
 
   const int nsteps = (hi - lo + TOK - 1) / TOK;
 
+  // Tokens at or past hi read the split's last token (a real, finite row);
+  // their scores are masked to -inf so they carry weight 0.
+  auto token_valid = [&](int step) { return lo + step * TOK + tg < hi; };
   auto load_slot = [&](int step) -> int32_t {
     const int32_t t = lo + step * TOK + tg;
-    return (step < nsteps && t < hi) ? idx[t] : -1;
+    return idx[t < hi ? t : hi - 1];
   };
 
   int step = wave;
@@ -193,7 +190,7 @@ split_attn_valu_kernel(AttnArgs a) {
     // Prefetch: next step's rows and the index two steps ahead.
     const Rows<CH> nxt = load_rows<CH, LPT>(kbase, vbase, row_stride16, ls, slot_nxt);
     const int32_t slot_nn = load_slot(step + 2 * kWaves);
-    const bool valid = slot_cur >= 0;
+    const bool valid = token_valid(step);
 
     // Scores (log2 units) for the G heads of this lane's token.
     float t[GP];

@@ -3,7 +3,7 @@
 // Same contract as the VALU path (AstrAI commit 0b661bae, workspace.py view:
 // per-split partials into decode_o_part / decode_ml_part); this file is the
 // CDNA4 design that moves both contractions onto MFMA so that the VALU only
-// does the softmax and the bf16 -> fp32 conversion of V.
+// does the softmax and packs operands.
 //
 // One workgroup (4 waves) per (request b, kv head g, split j); a wave takes
 // every 4th 16-token tile of the split.  Per tile:
@@ -19,11 +19,13 @@
 //   p       exp2(score * scale*log2(e) - mref) in place, with a per-head
 //           reference max that is only raised when a score exceeds it by more
 //           than kSlack (rare), and the true max tracked for the output.
-//   p.V     v_mfma_f32_16x16x4_f32: for token group i the A operand is lane
-//           l's p register i (A[head l%16][token 4k+i]) -- exactly where the
-//           score MFMA left it -- and the B operand is element e of a V row
-//           chunk loaded as lane l: token 4*(l/16)+i, chunk l%16 (whole rows
-//           per load instruction).  D/16 accumulators hold O[head][8n+e].
+//   p.V     v_mfma_f32_16x16x16_bf16: the A operand is lane l's four p values
+//           rounded to bf16 (A[head l%16][token 4*(l/16)+i]) -- exactly where
+//           the score MFMA left them.  V rows are loaded as lane l: token
+//           4*(l/16)+i, 16-byte chunk l%16 (whole rows per load instruction),
+//           and the B operand of column group e is element e of those four
+//           rows, packed with two byte permutes.  D/16 accumulators hold
+//           O[head][d = (D/16)*n + e].  The softmax sum uses p in fp32.
 // Two tiles of K/V are in flight per wave while the current one is used.
 #include "pd_internal.h"
 
@@ -32,31 +34,29 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+#ifndef PD_MFMA_MIN_WAVES_PER_EU
+#define PD_MFMA_MIN_WAVES_PER_EU 2
+#endif
 constexpr float kSlack = 8.0f;  // log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 template <int VE>
 struct VChunk;
 template <>
-struct VChunk<8> {  // D = 128: 16 bytes per lane per row
+struct VChunk<8> {  // D = 128: 16 bytes (8 bf16) of one V row per lane
   uint4 u;
-  __device__ static VChunk zero() { VChunk c; c.u = make_uint4(0, 0, 0, 0); return c; }
-  __device__ float el(int e) const {
-    const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
-    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-  }
+  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w; }
 };
 template <>
-struct VChunk<4> {  // D = 64: 8 bytes per lane per row
+struct VChunk<4> {  // D = 64: 8 bytes (4 bf16) of one V row per lane
   uint2 u;
-  __device__ static VChunk zero() { VChunk c; c.u = make_uint2(0, 0); return c; }
-  __device__ float el(int e) const {
-    const uint32_t w = e < 2 ? u.x : u.y;
-    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-  }
+  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : u.y; }
 };
 
 template <int D>
@@ -67,27 +67,23 @@ struct Tile {
   VChunk<VE> v[4];
 };
 
+// All loads are unconditional: every lane holds a valid slot (tokens past the
+// split's end were redirected to its last token), so the compiler can count
+// the loads in flight exactly and never drains the pipeline early.
 template <int D>
 __device__ __forceinline__ Tile<D> load_tile(const uint16_t* kl, const uint16_t* vl, int64_t stride,
                                              int32_t slot, int r, int c) {
   Tile<D> t;
   constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
+  const uint16_t* kp = kl + (int64_t)slot * stride + 8 * r;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) t.k[s] = make_uint4(0, 0, 0, 0);
-  if (slot >= 0) {
-    const uint16_t* kp = kl + (int64_t)slot * stride + 8 * r;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) t.k[s] = *reinterpret_cast<const uint4*>(kp + 32 * s);
-  }
+  for (int s = 0; s < KS; ++s) t.k[s] = *reinterpret_cast<const uint4*>(kp + 32 * s);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int32_t sv = __shfl(slot, 4 * r + i, 64);
-    t.v[i] = VChunk<VE>::zero();
-    if (sv >= 0) {
-      const uint16_t* vp = vl + (int64_t)sv * stride + VE * c;
-      if constexpr (VE == 8) t.v[i].u = *reinterpret_cast<const uint4*>(vp);
-      else t.v[i].u = *reinterpret_cast<const uint2*>(vp);
-    }
+    const uint16_t* vp = vl + (int64_t)sv * stride + VE * c;
+    if constexpr (VE == 8) t.v[i].u = *reinterpret_cast<const uint4*>(vp);
+    else t.v[i].u = *reinterpret_cast<const uint2*>(vp);
   }
   return t;
 }
@@ -104,7 +100,7 @@ __device__ inline void store_empty(const AttnArgs& a, int b, int g, int j, int D
 }
 
 template <int D, int GP>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, PD_MFMA_MIN_WAVES_PER_EU)
 split_attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -126,12 +122,12 @@ split_attn_mfma_kernel(AttnArgs a) {
   bf16x8_t qop[KS];
   {
     const int hq = c % GP;
+    const bool real = hq < a.group;
+    const uint16_t* qp = a.q + ((int64_t)b * a.n_heads + g * a.group + (real ? hq : 0)) * D + 8 * r;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (hq < a.group)
-        v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.n_heads + g * a.group + hq) * D +
-                                            8 * r + 32 * s);
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);  // unconditional load
+      if (!real) v = make_uint4(0, 0, 0, 0);
       qop[s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -147,9 +143,13 @@ split_attn_mfma_kernel(AttnArgs a) {
   const int32_t* idx = a.kv_indices + start;
   const int ntiles = (hi - lo + 15) >> 4;
 
+  // Slot of token c of a tile.  Tokens at or past hi (the tail of the last
+  // tile, and tiles past the end that are only prefetched) read the split's
+  // last token instead: a real row of this request, so finite, and its score
+  // is masked to -inf below, giving it weight 0.
   auto slot_of = [&](int tile) -> int32_t {
     const int32_t t = lo + tile * 16 + c;
-    return (tile < ntiles && t < hi) ? idx[t] : -1;
+    return idx[t < hi ? t : hi - 1];
   };
 
   auto compute = [&](const Tile<D>& T, int tile) {
@@ -180,18 +180,26 @@ split_attn_mfma_kernel(AttnArgs a) {
         for (int e = 0; e < VE; ++e) acc[e][jj] *= ar;
       }
     }
-    float p[4];
+    // p in fp32 for the softmax sum (exact lse); rounded to bf16 as the
+    // A operand of the p.V product.
+    bf16x4_t pb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mtrue = fmaxf(mtrue, t[i]);
-      p[i] = __builtin_amdgcn_exp2f(t[i] - mref);
-      lsum += p[i];
+      const float p = __builtin_amdgcn_exp2f(t[i] - mref);
+      lsum += p;
+      pb[i] = (__bf16)p;
     }
+    const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
+    // B operand for column group e: element e of the lane's 4 token rows,
+    // packed pairwise with byte permutes (low or high bf16 of a dword).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int e = 0; e < VE; ++e)
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], T.v[i].el(e), acc[e], 0, 0, 0);
+    for (int e = 0; e < VE; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2_t bv;
+      bv[0] = __builtin_amdgcn_perm(T.v[1].dw(e >> 1), T.v[0].dw(e >> 1), sel);
+      bv[1] = __builtin_amdgcn_perm(T.v[3].dw(e >> 1), T.v[2].dw(e >> 1), sel);
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv), acc[e], 0, 0, 0);
     }
   };
 

@@ -64,18 +64,30 @@ merge_kernel(MergeArgs a) {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 64);
       wsum += ws;
+      // Rows in batches of 8 with unconditional loads (indices clamped to the
+      // last split, whose weight is then 0), so the loads overlap.
       const int n = min(64, a.num_splits - j0);
-      for (int jj = 0; jj < n; ++jj) {
-        const float wj = __shfl(w, jj, 64);
-        if (wj == 0.f) continue;  // wave-uniform: empty split
-        const float* row = op + (int64_t)(j0 + jj) * D + lane * E;
-        if (E == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(row);
-          acc[0] = fmaf(wj, v.x, acc[0]);
-          acc[E - 1] = fmaf(wj, v.y, acc[E - 1]);
-        } else {
+      for (int jb = 0; jb < n; jb += 8) {
+        float v[8][E];
+        float wj[8];
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] = fmaf(wj, row[e], acc[e]);
+        for (int u = 0; u < 8; ++u) {
+          const int jj = jb + u < n ? jb + u : n - 1;
+          wj[u] = jb + u < n ? __shfl(w, jj, 64) : 0.f;
+          const float* row = op + (int64_t)(j0 + jj) * D + lane * E;
+          if constexpr (E == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(row);
+            v[u][0] = t.x;
+            v[u][E - 1] = t.y;
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[u][e] = row[e];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = fmaf(wj[u], wj[u] == 0.f ? 0.f : v[u][e], acc[e]);
         }
       }
     }

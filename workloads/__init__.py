@@ -83,13 +83,15 @@ def _fill_store(gen, n_layers, num_slots, hkv, d, chunk_rows=1 << 16):
 def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim,
                 page_size=16, num_pages=None, pool_factor=1.25, growth=0,
                 max_pages_per_req=None, q_scale=1.0, scale=None,
-                nan_unassigned=True, seq_lens_drawn=None):
+                nan_unassigned=True, shuffle=True):
     """Build a workload.
 
     ``seq_lens`` is either a list of ints or a callable ``gen -> list`` that
     draws them (so that the draw happens first, from the seeded generator).
     ``growth`` reserves pages for that many future tokens per request (decode
     steps that add one token each), so steady-state steps need no new pages.
+    ``shuffle=False`` assigns pages in order instead of by the seeded
+    permutation (a locality experiment; the named workloads shuffle).
     """
     gen = torch.Generator().manual_seed(seed)
     lens = list(seq_lens(gen)) if callable(seq_lens) else list(seq_lens)
@@ -101,6 +103,8 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
     if num_pages < total_pages:
         raise ValueError("pool too small for the requested lengths")
     perm = torch.randperm(num_pages, generator=gen).to(torch.int32)
+    if not shuffle:  # contiguous page assignment (same draw order, permutation unused)
+        perm = torch.arange(num_pages, dtype=torch.int32)
     mppr = max_pages_per_req if max_pages_per_req is not None else max(1, max(pages_b))
     if mppr < max(pages_b):
         raise ValueError("max_pages_per_req smaller than a request's page count")
