@@ -91,15 +91,18 @@ typedef struct pd_layout {
   size_t arena_bytes;
   size_t kv_indptr;   /* int32 [max_batch + 1]                                 */
   size_t kv_indices;  /* int32 [max_total_tokens]                              */
+  size_t page_indptr; /* int32 [max_batch + 1]: prefix sum of ceil(L_b / page_size)
+                         (pages per request, used by the split plan)           */
   size_t o_part;      /* fp32  [max_batch, n_heads, max_splits, head_dim]:
                          each split's output normalised by its own softmax sum
                          ([WS] decode_o_part)                                  */
   size_t ml_part;     /* fp32  [max_batch, n_heads, max_splits, 2]: (m, ln l)
                          with m the split's max scaled score and
                          l = sum exp(s - m); lse = m + ln l; an empty split
-                         holds (-inf, -inf) ([WS] decode_ml_part)              */
+                         holds (-inf, -inf) and its o_part row is
+                         unspecified ([WS] decode_ml_part)                     */
   size_t meta;        /* int32 [16]: [0] = max pages of any request this step,
-                         [1] = total tokens this step                          */
+                         [1] = total tokens, [2] = total pages this step       */
   size_t error_word;  /* uint32: PD_ERR_* bits                                 */
 } pd_layout;
 
@@ -120,8 +123,9 @@ pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena,
 pd_status paged_decode_layout(const pd_handle* h, pd_layout* out);
 
 /* Resolves the split count S for a batch: requested > 0 is honoured (it must be
- * <= max_splits); requested == 0 picks one from batch x n_kv_heads against the
- * device's compute units (and max_pages_per_req, so a split keeps >= 4 pages).
+ * <= max_splits); requested == 0 picks S = 1 + ceil(4096 / (batch*n_kv_heads)),
+ * capped at max_splits and max_pages_per_req (at least 2), so that the split
+ * plan below can give all 2048 chunks the same number of pages.
  * Pass the same S to paged_decode_attn and paged_decode_merge. */
 pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t requested,
                                   int32_t* num_splits);
@@ -144,9 +148,17 @@ pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* 
  *   d_k_store  bf16 [n_layers, num_slots, n_kv_heads, head_dim] (base of the
  *   d_v_store  whole store; the library adds the 64-bit offset of `layer`)
  *   scale      softmax scale applied to q.k (float32)
- * Split j of request b covers pages [j*c, (j+1)*c) with
- * c = max(1, ceil(max_b ceil(L_b/page_size) / S)); splits past a request's end
- * are written as empty.  Reads kv_indptr / kv_indices from the last bind. */
+ * Split plan (S = num_splits, P_b = ceil(L_b / page_size)): the rows
+ * (request b, kv head g) are laid end to end, request-major, each as its P_b
+ * pages.  S = 1: each row is one split.  S >= 2: the page sequence is cut
+ * into chunks of Qp = max(ceil(TP / 2048), ceil(P_max / (S - 1)), 1) pages
+ * (TP = n_kv_heads * sum P_b, P_max = max P_b), and split j of row (b, g) is
+ * the row's intersection with the j-th chunk that touches it -- a contiguous,
+ * page-aligned token range; a row never has more than S splits.  For every
+ * query head h of kv head g, o_part[b,h,j,:] and ml_part[b,h,j,:] describe
+ * split j; splits past a row's last one are empty: ml = (-inf, -inf) and
+ * o_part is left unspecified.  Reads kv_indptr / kv_indices / page_indptr
+ * from the last bind.  One launch of 512 workgroups (2048 waves). */
 pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
                             const void* d_q, const void* d_k_store, const void* d_v_store,
                             float scale, hipStream_t stream);

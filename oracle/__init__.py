@@ -27,8 +27,9 @@ from .paged_attention import (  # noqa: F401
     kv_indices,
     kv_indptr,
     merge_splits,
-    pages_per_split,
+    SPLIT_CHUNKS,
+    chunk_pages,
     split_partials,
-    split_token_ranges,
+    split_plan,
     to_f64,
 )

@@ -15,9 +15,15 @@ bullets and print no formulas):
   * The single new query attends to all L_b cached tokens, its own included;
     there is no mask ([CA] bullets dropping decode_mask / page_table).
   * Softmax is natural-base; ``scale`` is the float32 value the kernel gets.
-  * Split partition: with P_max = max_b P_b and c = max(1, ceil(P_max / S))
-    pages per split, split j of request b covers pages [j*c, (j+1)*c) clipped
-    to P_b; splits past the end are empty.
+  * Split partition (the pages fix no rule; any partition yields the same
+    merged output).  The rows (request b, kv head g) are laid end to end,
+    request-major, each as its P_b pages.  With S = 1 every non-empty row is
+    one split.  With S >= 2 that page sequence is cut into chunks of
+    Qp = max(ceil(TP / 2048), ceil(P_max / (S - 1)), 1) pages (TP = total
+    pages of all rows); split j of a row is its intersection with the j-th
+    chunk that touches it.  A row then never has more than S splits, and
+    every chunk holds the same number of pages.  Splits past a row's last
+    chunk are empty.
   * Per-split outputs ([WS] bullet on decode_o_part / decode_ml_part): o_j is
     normalised by its own softmax sum; the (m, log-sum) pair is
     m_j = max score, ln l_j with l_j = sum exp(s - m_j), so lse_j = m_j + ln l_j.
@@ -147,29 +153,57 @@ def decode_attention(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale
 # decode_o_part / decode_ml_part and the split partial buffers).
 # --------------------------------------------------------------------------
 
-def pages_per_split(seq_lens, page_size, S):
-    """c = max(1, ceil(P_max / S)) with P_max = max_b ceil(L_b / ps)."""
-    p_max = max([-(-int(x) // page_size) for x in np.asarray(seq_lens).reshape(-1)] + [0])
-    return max(1, -(-p_max // int(S)))
+SPLIT_CHUNKS = 2048  # the page sequence is cut into at most this many chunks
 
 
-def split_token_ranges(L_b, page_size, S, c):
-    """Token range [lo, hi) of each split of one request (hi <= lo means empty)."""
-    ranges = []
-    for j in range(S):
-        lo = j * c * page_size
-        hi = min((j + 1) * c * page_size, int(L_b))
-        ranges.append((lo, max(lo, hi)))
-    return ranges
+def _pages(seq_lens, page_size):
+    return [-(-int(x) // page_size) for x in np.asarray(seq_lens).reshape(-1)]
+
+
+def chunk_pages(seq_lens, page_size, n_kv_heads, S, n_chunks=SPLIT_CHUNKS):
+    """Qp for S >= 2: max(ceil(TP / n_chunks), ceil(P_max / (S - 1)), 1)."""
+    P = _pages(seq_lens, page_size)
+    tp = n_kv_heads * sum(P)
+    p_max = max(P + [0])
+    return max(-(-tp // n_chunks), -(-p_max // (int(S) - 1)), 1)
+
+
+def split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks=SPLIT_CHUNKS):
+    """Token ranges of the splits: plan[b][g] = [(lo, hi), ...] indexed by j.
+
+    Walks the rows in order, page by page, and starts a new split whenever the
+    chunk index of the global page changes (S >= 2) or a row begins.
+    """
+    L = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
+    P = _pages(L, page_size)
+    plan = [[[] for _ in range(n_kv_heads)] for _ in L]
+    qp = None if int(S) == 1 else chunk_pages(L, page_size, n_kv_heads, S, n_chunks)
+    gp = 0  # global page index of the current page
+    for b, lb in enumerate(L):
+        for g in range(n_kv_heads):
+            cur = None  # (chunk id, first local page)
+            for lp in range(P[b]):
+                k = 0 if qp is None else gp // qp
+                if cur is None or k != cur[0]:
+                    if cur is not None:
+                        plan[b][g].append((cur[1] * page_size, min(lp * page_size, lb)))
+                    cur = (k, lp)
+                gp += 1
+            if cur is not None:
+                plan[b][g].append((cur[1] * page_size, lb))
+    return plan
 
 
 def split_partials(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale,
                    n_kv_heads, page_size, S, pairs=None):
-    """Per-split outputs: o [B, H, S, D], m [B, H, S], lse [B, H, S] (float64)."""
+    """Per-split outputs: o [B, H, S, D], m [B, H, S], lse [B, H, S] (float64).
+
+    Empty splits: o = 0, m = lse = -inf.
+    """
     q = to_f64(q_layer)
     B, H, D = q.shape
     G = H // n_kv_heads
-    c = pages_per_split(seq_lens, page_size, S)
+    plan = split_plan(seq_lens, page_size, n_kv_heads, S)
     o = np.full((B, H, S, D), np.nan)
     m = np.full((B, H, S), np.nan)
     lse = np.full((B, H, S), np.nan)
@@ -177,7 +211,10 @@ def split_partials(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale,
         pairs = [(b, g) for b in range(B) for g in range(n_kv_heads)]
     for b, g in pairs:
         slots_b = indices[indptr[b]:indptr[b + 1]]
-        for j, (lo, hi) in enumerate(split_token_ranges(seq_lens[b], page_size, S, c)):
+        ranges = plan[b][g]
+        assert len(ranges) <= S, "more splits than S"
+        for j in range(S):
+            lo, hi = ranges[j] if j < len(ranges) else (0, 0)
             K = gather_rows(k_layer[:, g], slots_b[lo:hi])
             V = gather_rows(v_layer[:, g], slots_b[lo:hi])
             for h in range(g * G, (g + 1) * G):

@@ -51,7 +51,7 @@ class PdConfig(ctypes.Structure):
 
 class PdLayout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_size_t) for name in (
-        "arena_bytes", "kv_indptr", "kv_indices", "o_part", "ml_part", "meta", "error_word")]
+        "arena_bytes", "kv_indptr", "kv_indices", "page_indptr", "o_part", "ml_part", "meta", "error_word")]
 
 
 class PagedDecodeError(RuntimeError):

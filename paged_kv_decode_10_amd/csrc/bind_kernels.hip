@@ -63,21 +63,34 @@ bind_scan_kernel(BindArgs a) {
   const int64_t lo = min(excl, a.max_total_tokens);
   const int64_t hi = min(excl + len, a.max_total_tokens);
   if (b < a.batch && hi - lo < len) flags |= PD_ERR_TOTAL_OVER_CAP;
-  const int pages = (int)((hi - lo + a.page_size - 1) / a.page_size);
+  if (b == a.batch - 1) a.meta[kMetaTotalTokens] = (int32_t)hi;
+  const int pages = (b < a.batch) ? (int)((hi - lo + a.page_size - 1) / a.page_size) : 0;
   if (b < a.batch) {
     a.kv_indptr[b + 1] = (int32_t)hi;
     if (b == 0) a.kv_indptr[0] = 0;
   }
-  int mp = wave_max_int(b < a.batch ? pages : 0);
+  int mp = wave_max_int(pages);
+  // Second scan: page counts (the split plan walks rows page by page).
+  const int64_t pincl = wave_inclusive_scan(pages);
+  __syncthreads();  // wave_tot is reused
+  if (lane == 63) wave_tot[wave] = pincl;
   if (lane == 0) wave_maxp[wave] = mp;
   __syncthreads();
+  int64_t pbefore = 0;
+  for (int w = 0; w < wave; ++w) pbefore += wave_tot[w];
+  if (b < a.batch) {
+    a.page_indptr[b + 1] = (int32_t)(pbefore + pincl);
+    if (b == 0) a.page_indptr[0] = 0;
+  }
   if (b == 0) {
     int m = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) m = max(m, wave_maxp[w]);
+    int64_t ptotal = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      m = max(m, wave_maxp[w]);
+      ptotal += wave_tot[w];
+    }
     a.meta[kMetaMaxPages] = m;
-    int64_t total = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) total += wave_tot[w];
-    a.meta[kMetaTotalTokens] = (int32_t)min(total, a.max_total_tokens);
+    a.meta[kMetaTotalPages] = (int32_t)ptotal;
   }
   if (flags) atomicOr(a.error_word, flags);
 }

@@ -8,7 +8,8 @@
 //
 // One wave per (request, query head): lane j reads split j's statistics, the
 // wave reduces max and sum with shuffles, then every lane accumulates its
-// D/64 columns over the non-empty splits (one coalesced row load per split).
+// D/64 columns over the non-empty splits (one coalesced row load per split,
+// the loads of a batch issued together).
 #include "pd_internal.h"
 
 namespace pd {
@@ -23,10 +24,41 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+template <int D, int NB>
+__device__ __forceinline__ void load_rows(const float* op, int j0, int n, int lane, float (&v)[NB][D / 64]) {
+  constexpr int E = D / 64;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int jj = j0 + (u < n ? u : n - 1);
+    const float* row = op + (int64_t)jj * D + lane * E;
+    if constexpr (E == 2) {
+      const float2 t = *reinterpret_cast<const float2*>(row);
+      v[u][0] = t.x;
+      v[u][E - 1] = t.y;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[u][e] = row[e];
+    }
+  }
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void accumulate(float (&acc)[D / 64], const float (&v)[NB][D / 64], float w,
+                                           int u0, int n) {
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const float wj = u < n ? __shfl(w, u0 + u, 64) : 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = wj == 0.f ? acc[e] : fmaf(wj, v[u][e], acc[e]);
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(kMergeWaves * 64)
 merge_kernel(MergeArgs a) {
   constexpr int E = D / 64;  // columns per lane
+  constexpr int kSpec = 8;   // split rows read together with the statistics
+  constexpr int kBatch = 16;
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (item >= a.batch * a.n_heads) return;
@@ -34,18 +66,31 @@ merge_kernel(MergeArgs a) {
   const float* ml = a.ml_part + base * 2;
   const float* op = a.o_part + base * D;
 
-  // Pass 1: max of lse over splits.
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < a.num_splits; j0 += 64) {
+  // One round trip for the common case: the statistics of the first 64
+  // splits (lane j holds split j) and, speculatively, the rows of the first
+  // kSpec splits.  An empty split's row is unspecified data; its weight is 0
+  // and it is never added.
+  const int s0 = a.num_splits < 64 ? a.num_splits : 64;
+  float lse = -INFINITY;
+  if (lane < s0) {
+    const float m = ml[2 * lane], ln_l = ml[2 * lane + 1];
+    lse = (m == -INFINITY) ? -INFINITY : m + ln_l;
+  }
+  float spec[kSpec][E];
+  load_rows<D, kSpec>(op, 0, s0 < kSpec ? s0 : kSpec, lane, spec);
+  float M = lse;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  for (int j0 = 64; j0 < a.num_splits; j0 += 64) {  // more than 64 splits (rare)
     const int j = j0 + lane;
-    float lse = -INFINITY;
+    float l2 = -INFINITY;
     if (j < a.num_splits) {
       const float m = ml[2 * j], ln_l = ml[2 * j + 1];
-      lse = (m == -INFINITY) ? -INFINITY : m + ln_l;
+      l2 = (m == -INFINITY) ? -INFINITY : m + ln_l;
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lse = fmaxf(lse, __shfl_xor(lse, off, 64));
-    M = fmaxf(M, lse);
+    for (int off = 32; off >= 1; off >>= 1) l2 = fmaxf(l2, __shfl_xor(l2, off, 64));
+    M = fmaxf(M, l2);
   }
 
   float acc[E];
@@ -56,7 +101,9 @@ merge_kernel(MergeArgs a) {
     for (int j0 = 0; j0 < a.num_splits; j0 += 64) {
       const int j = j0 + lane;
       float w = 0.f;
-      if (j < a.num_splits) {
+      if (j0 == 0) {
+        w = lse == -INFINITY ? 0.f : __expf(lse - M);
+      } else if (j < a.num_splits) {
         const float m = ml[2 * j], ln_l = ml[2 * j + 1];
         w = (m == -INFINITY) ? 0.f : __expf(m + ln_l - M);
       }
@@ -64,31 +111,17 @@ merge_kernel(MergeArgs a) {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 64);
       wsum += ws;
-      // Rows in batches of 8 with unconditional loads (indices clamped to the
-      // last split, whose weight is then 0), so the loads overlap.
-      const int n = min(64, a.num_splits - j0);
-      for (int jb = 0; jb < n; jb += 8) {
-        float v[8][E];
-        float wj[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int jj = jb + u < n ? jb + u : n - 1;
-          wj[u] = jb + u < n ? __shfl(w, jj, 64) : 0.f;
-          const float* row = op + (int64_t)(j0 + jj) * D + lane * E;
-          if constexpr (E == 2) {
-            const float2 t = *reinterpret_cast<const float2*>(row);
-            v[u][0] = t.x;
-            v[u][E - 1] = t.y;
-          } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) v[u][e] = row[e];
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] = fmaf(wj[u], wj[u] == 0.f ? 0.f : v[u][e], acc[e]);
-        }
+      const uint64_t nonempty = __builtin_amdgcn_ballot_w64(w != 0.f);
+      const int n = 64 - __clzll(nonempty);  // one past the last non-empty split
+      int jb = 0;
+      if (j0 == 0) {
+        accumulate<D, kSpec>(acc, spec, w, 0, n < kSpec ? n : kSpec);
+        jb = kSpec;
+      }
+      for (; jb < n; jb += kBatch) {
+        float v[kBatch][E];
+        load_rows<D, kBatch>(op, j0 + jb, n - jb, lane, v);
+        accumulate<D, kBatch>(acc, v, w, jb, n - jb);
       }
     }
   }

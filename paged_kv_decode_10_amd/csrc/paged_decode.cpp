@@ -55,6 +55,8 @@ pd_layout make_layout(const pd_config* c) {
   off = align_up(off + (size_t)(c->max_batch + 1) * 4);
   l.kv_indices = off;
   off = align_up(off + (size_t)c->max_total_tokens * 4);
+  l.page_indptr = off;
+  off = align_up(off + (size_t)(c->max_batch + 1) * 4);
   const size_t rows = (size_t)c->max_batch * c->n_heads * c->max_splits;
   l.o_part = off;
   off = align_up(off + rows * c->head_dim * 4);
@@ -76,18 +78,6 @@ T* at(const pd_handle* h, size_t off) {
 pd_status hip_status(hipError_t e) { return e == hipSuccess ? PD_OK : PD_E_HIP; }
 
 }  // namespace
-
-namespace pd {
-// The matrix-core kernel is the default; building with -DPD_ATTN_VALU selects
-// the VALU kernel instead (for comparisons).
-hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream) {
-#ifdef PD_ATTN_VALU
-  return launch_attn_valu(a, head_dim, stream);
-#else
-  return launch_attn_mfma(a, head_dim, stream);
-#endif
-}
-}  // namespace pd
 
 extern "C" {
 
@@ -122,6 +112,8 @@ pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena, size_
   // Start from an empty step: zero kv_indptr, meta and the error word so an
   // attention call before the first bind sees no tokens.
   hipError_t e = hipMemsetAsync(h->arena + lay.kv_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(h->arena + lay.page_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.meta, 0, 16 * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.error_word, 0, 4, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
@@ -148,16 +140,14 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t req
     *num_splits = requested;
     return PD_OK;
   }
-  // About eight 4-wave workgroups per compute unit over batch x kv heads, but
-  // no finer than 4 pages per split for a full-length request.
-  const int64_t target = 8LL * h->num_cus;
-  const int64_t per = (int64_t)batch * h->cfg.n_kv_heads;
-  int64_t S = (target + per - 1) / per;
-  int64_t by_len = h->cfg.max_pages_per_req / 4;
-  if (by_len < 1) by_len = 1;
-  if (S > by_len) S = by_len;
+  // The plan cuts the page sequence into 2048 equal chunks when no row needs
+  // more than S splits for it; rows average 2048 / (batch * n_kv_heads) chunks,
+  // so allow about twice that.  More splits than pages buys nothing.
+  const int64_t rows = (int64_t)batch * h->cfg.n_kv_heads;
+  int64_t S = 1 + (2LL * pd::kSplitChunks + rows - 1) / rows;
+  if (S > h->cfg.max_pages_per_req) S = h->cfg.max_pages_per_req;
   if (S > h->cfg.max_splits) S = h->cfg.max_splits;
-  if (S < 1) S = 1;
+  if (S < 2) S = h->cfg.max_splits >= 2 ? 2 : 1;
   *num_splits = (int32_t)S;
   return PD_OK;
 }
@@ -184,6 +174,7 @@ pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* 
   a.req_to_page = d_req_to_page;
   a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
   a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
+  a.page_indptr = at<int32_t>(h, h->lay.page_indptr);
   a.meta = at<int32_t>(h, h->lay.meta);
   a.error_word = at<uint32_t>(h, h->lay.error_word);
   return hip_status(pd::launch_bind(a, stream));
@@ -214,6 +205,7 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
   a.v_layer = static_cast<const uint16_t*>(d_v_store) + (int64_t)layer * layer_elems;
   a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
   a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
+  a.page_indptr = at<int32_t>(h, h->lay.page_indptr);
   a.meta = at<int32_t>(h, h->lay.meta);
   a.o_part = at<float>(h, h->lay.o_part);
   a.ml_part = at<float>(h, h->lay.ml_part);

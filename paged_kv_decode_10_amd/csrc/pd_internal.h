@@ -13,7 +13,12 @@ namespace pd {
 enum MetaWord : int {
   kMetaMaxPages = 0,     // max over requests of ceil(L_b / page_size)
   kMetaTotalTokens = 1,  // sum of the (clamped) lengths
+  kMetaTotalPages = 2,   // sum over requests of ceil(L_b / page_size)
 };
+
+// The split plan cuts the page sequence of all (request, kv head) rows into
+// at most this many equal chunks; the attention launches one wave per chunk.
+constexpr int kSplitChunks = 2048;
 
 struct BindArgs {
   int32_t batch;
@@ -27,6 +32,7 @@ struct BindArgs {
   const int32_t* req_to_page;
   int32_t* kv_indptr;
   int32_t* kv_indices;
+  int32_t* page_indptr;       // [batch + 1]: prefix sum of ceil(L_b / page_size)
   int32_t* meta;
   uint32_t* error_word;
 };
@@ -45,6 +51,7 @@ struct AttnArgs {
   const uint16_t* v_layer;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
+  const int32_t* page_indptr;
   const int32_t* meta;
   float* o_part;              // [max_batch, n_heads, max_splits, D]
   float* ml_part;             // [max_batch, n_heads, max_splits, 2]
@@ -61,9 +68,6 @@ struct MergeArgs {
 };
 
 hipError_t launch_bind(const BindArgs& a, hipStream_t stream);
-// Split attention kernels: VALU (dot2 + DPP) and matrix-core variants.
-hipError_t launch_attn_valu(const AttnArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_attn_mfma(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 

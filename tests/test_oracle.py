@@ -240,11 +240,52 @@ def test_page_permutation_invariance_bit_exact():
 
 def test_split_plan_golden():
     g = _load("split_example.json")
-    c = oracle.pages_per_split(g["seq_lens"], g["page_size"], g["num_splits"])
-    assert c == g["pages_per_split"]
-    for b, L in enumerate(g["seq_lens"]):
-        r = oracle.split_token_ranges(L, g["page_size"], g["num_splits"], c)
-        assert [list(x) for x in r] == g["ranges"][b]
+    for S, want in g["plans"].items():
+        plan = oracle.split_plan(g["seq_lens"], g["page_size"], g["n_kv_heads"], int(S))
+        got = [[[list(r) for r in plan[b][h]] for h in range(g["n_kv_heads"])] for b in range(2)]
+        assert got == want, S
+
+
+def _brute_plan(L, ps, hkv, S, n_chunks):
+    """Same rule, computed another way: chunk id of every (row, page) pair, then
+    group each row's pages by chunk id."""
+    P = [-(-x // ps) for x in L]
+    rows = [(b, g) for b in range(len(L)) for g in range(hkv)]
+    flat = [(b, g, lp) for (b, g) in rows for lp in range(P[b])]
+    if S == 1:
+        cid = [rows.index((b, g)) for (b, g, lp) in flat]
+    else:
+        tp, pm = len(flat), max(P + [0])
+        qp = max(math.ceil(tp / n_chunks), math.ceil(pm / (S - 1)), 1)
+        cid = [i // qp for i in range(len(flat))]
+    out = {}
+    for (b, g, lp), k in zip(flat, cid):
+        out.setdefault((b, g), {}).setdefault(k, []).append(lp)
+    plan = [[[] for _ in range(hkv)] for _ in L]
+    for (b, g), groups in out.items():
+        for k in sorted(groups):
+            pages = groups[k]
+            plan[b][g].append((pages[0] * ps, min((pages[-1] + 1) * ps, L[b])))
+    return plan
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_split_plan_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    ps = int(rng.choice([1, 3, 16]))
+    L = [int(x) for x in rng.integers(0, 90, size=int(rng.integers(1, 6)))]
+    hkv = int(rng.integers(1, 4))
+    for S in (1, 2, 3, 5, 9):
+        for nc in (2, 7, 2048):
+            got = oracle.split_plan(L, ps, hkv, S, n_chunks=nc)
+            assert got == _brute_plan(L, ps, hkv, S, nc), (S, nc)
+            for b in range(len(L)):
+                for g in range(hkv):
+                    rr = got[b][g]
+                    assert len(rr) <= S
+                    assert sum(hi - lo for lo, hi in rr) == L[b]
+                    assert all(lo % ps == 0 and lo < hi for lo, hi in rr)
+                    assert all(rr[i][1] == rr[i + 1][0] for i in range(len(rr) - 1))
 
 
 @pytest.mark.parametrize("S", [1, 2, 4, 7, 32])
@@ -258,13 +299,14 @@ def test_split_invariance_and_merge_identity(S):
     mo, mlse = oracle.merge_splits(o, lsep)
     np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(mlse, lse, rtol=0, atol=1e-12)
-    # partition covers each request exactly once
-    c = oracle.pages_per_split(L, w.page_size, S)
+    # partition covers each (request, kv head) exactly once
+    plan = oracle.split_plan(L, w.page_size, w.n_kv_heads, S)
     for b in range(w.batch):
-        rr = oracle.split_token_ranges(L[b], w.page_size, S, c)
-        assert sum(hi - lo for lo, hi in rr) == L[b]
-        for lo, hi in rr:
-            assert lo % w.page_size == 0
+        for g in range(w.n_kv_heads):
+            rr = plan[b][g]
+            assert sum(hi - lo for lo, hi in rr) == L[b] and len(rr) <= S
+            for lo, hi in rr:
+                assert lo % w.page_size == 0
     # empty splits
     empty = ~np.isfinite(lsep)
     assert np.all(np.isneginf(lsep[empty])) and np.all(np.isneginf(m[empty]))
@@ -280,19 +322,19 @@ def test_split_partial_equals_attention_over_its_range():
     o, m, lse = oracle.split_partials(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale,
                                       w.n_kv_heads, w.page_size, S)
     G = w.group
-    c = oracle.pages_per_split(L, w.page_size, S)
+    plan = oracle.split_plan(L, w.page_size, w.n_kv_heads, S)
     for b in range(w.batch):
-        for j, (lo, hi) in enumerate(oracle.split_token_ranges(L[b], w.page_size, S, c)):
-            if hi <= lo:
-                continue
-            slots = torch.from_numpy(ix[ip[b] + lo: ip[b] + hi])
-            K = w.k_store[0, slots].to(torch.float64).permute(1, 0, 2).repeat_interleave(G, 0)
-            V = w.v_store[0, slots].to(torch.float64).permute(1, 0, 2).repeat_interleave(G, 0)
-            qb = w.q[0, b].to(torch.float64).unsqueeze(1)
-            ref = torch.nn.functional.scaled_dot_product_attention(qb, K, V, scale=w.scale)[:, 0]
-            np.testing.assert_allclose(o[b, :, j], ref.numpy(), atol=1e-12, rtol=0)
-            smax = (w.scale * torch.einsum("hld,hd->hl", K, w.q[0, b].to(torch.float64))).max(-1).values
-            np.testing.assert_allclose(m[b, :, j], smax.numpy(), atol=1e-12, rtol=0)
+        for g in range(w.n_kv_heads):
+            hs = slice(g * G, (g + 1) * G)
+            for j, (lo, hi) in enumerate(plan[b][g]):
+                slots = torch.from_numpy(ix[ip[b] + lo: ip[b] + hi])
+                K = w.k_store[0, slots, g].to(torch.float64).unsqueeze(0).expand(G, -1, -1)
+                V = w.v_store[0, slots, g].to(torch.float64).unsqueeze(0).expand(G, -1, -1)
+                qb = w.q[0, b, hs].to(torch.float64).unsqueeze(1)
+                ref = torch.nn.functional.scaled_dot_product_attention(qb, K, V, scale=w.scale)[:, 0]
+                np.testing.assert_allclose(o[b, hs, j], ref.numpy(), atol=1e-12, rtol=0)
+                smax = (w.scale * torch.einsum("hld,hd->hl", K, w.q[0, b, hs].to(torch.float64))).max(-1).values
+                np.testing.assert_allclose(m[b, hs, j], smax.numpy(), atol=1e-12, rtol=0)
 
 
 def test_merge_weights_by_lse():
