@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attn: KV HBM GB/s (% of peak) and µs/layer at B=1..32"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
-ATTN_SOURCES = ("paged_kv_decode_10_amd/csrc/attn_mfma.hip", "paged_kv_decode_10_amd/csrc/attn_kernels.hip",
-                "paged_kv_decode_10_amd/csrc/pd_internal.h", "paged_kv_decode_10_amd/csrc/paged_decode.cpp")
+ATTN_SOURCES = ("paged_kv_decode_10_amd/csrc/attn_split.hip", "paged_kv_decode_10_amd/csrc/pd_internal.h",
+                "paged_kv_decode_10_amd/csrc/paged_decode.cpp")
 
 
 def log(*a):
@@ -47,13 +47,34 @@ def attn_kernel_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def attn_bytes(seq_lens, n_kv_heads, head_dim, batch, n_heads, num_splits):
-    """Algorithmic bytes of one attention launch: K+V rows, kv_indices, q, partial writes."""
+def split_segments(seq_lens, page_size, n_kv_heads, num_splits, chunks=2048):
+    """Number of non-empty (request, kv head, split) partials the split plan
+    writes: a row of P pages starting at global page G meets the chunks
+    floor(G/Qp) .. floor((G+P-1)/Qp) (one split per row when S = 1)."""
+    import numpy as np
+
+    P = (np.asarray(seq_lens, dtype=np.int64) + page_size - 1) // page_size
+    if num_splits == 1:
+        return int((P > 0).sum()) * n_kv_heads
+    tp = int(P.sum()) * n_kv_heads
+    qp = max(-(-tp // chunks), -(-int(P.max()) // (num_splits - 1)), 1)
+    G = (np.concatenate([[0], np.cumsum(P)[:-1]])[:, None] * n_kv_heads
+         + np.arange(n_kv_heads)[None, :] * P[:, None])
+    Pr = np.repeat(P[:, None], n_kv_heads, axis=1)
+    n = np.where(Pr > 0, (G + Pr - 1) // qp - G // qp + 1, 0)
+    return int(n.sum())
+
+
+def attn_bytes(seq_lens, n_kv_heads, head_dim, batch, n_heads, num_splits, page_size):
+    """Algorithmic bytes of one attention launch: the K and V rows of every
+    cached token, the kv_indices list, q, and the partials of the non-empty
+    splits (o row fp32 + (m, ln l) per query head)."""
     tok = int(seq_lens.sum())
     kv = tok * n_kv_heads * head_dim * 2 * 2
     idx = tok * 4
     q = batch * n_heads * head_dim * 2
-    parts = batch * n_heads * num_splits * (head_dim * 4 + 8)
+    group = n_heads // n_kv_heads
+    parts = split_segments(seq_lens, page_size, n_kv_heads, num_splits) * group * (head_dim * 4 + 8)
     return kv, kv + idx + q + parts
 
 
@@ -199,20 +220,23 @@ def main() -> int:
     torch.cuda.synchronize()
     attn_us = e0.elapsed_time(e1) * 1e3 / (R * NL)
     Lnow = seq.cpu().to(torch.int64)
-    kv_l, alg_l = attn_bytes(Lnow, Hkv, D, B, H, S)
+    kv_l, alg_l = attn_bytes(Lnow, Hkv, D, B, H, S, w.page_size)
     achieved = alg_l / (attn_us * 1e-6) / 1e9
     log(f"[bench] attention kernel: {attn_us:.2f} us/launch, {alg_l / 1e6:.1f} MB algorithmic "
         f"({kv_l / 1e6:.1f} MB KV) -> {achieved:.0f} GB/s")
+    # HBM traffic per launch from the committed counter summary, valid only
+    # for the same kernel sources and the same launch (split count, KV bytes).
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_digest") == attn_kernel_digest() and tr.get("splits") == S:
+        if (tr.get("kernel_digest") == attn_kernel_digest() and tr.get("splits") == S
+                and tr.get("kv_bytes_per_launch") == kv_l):
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "split_attn (paged_decode_attn)", "us_per_launch": round(attn_us, 3),
-                "algorithmic_bytes_per_launch": alg_l}
+                "kernel": "split_attn_kernel<128,4> (paged_decode_attn)", "us_per_launch": round(attn_us, 3),
+                "algorithmic_bytes_per_launch": alg_l, "kv_bytes_per_launch": kv_l}
 
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
