@@ -47,22 +47,32 @@ def attn_kernel_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def split_segments(seq_lens, page_size, n_kv_heads, num_splits, chunks=2048):
-    """Number of non-empty (request, kv head, split) partials the split plan
-    writes: a row of P pages starting at global page G meets the chunks
-    floor(G/Qp) .. floor((G+P-1)/Qp) (one split per row when S = 1)."""
+def row_splits(seq_lens, page_size, n_kv_heads, num_splits, chunks=2048):
+    """Splits of every (request, kv head) row under the launch's plan.  Kv
+    heads form bundles of T = gcd(n_kv_heads, 4); a bundle row of P pages
+    starting at global page G meets the chunks floor(G/Qp) .. floor((G+P-1)/Qp)
+    of 2048/T chunks (one split per non-empty row when S = 1)."""
+    import math
+
     import numpy as np
 
+    team = math.gcd(n_kv_heads, 4)
+    hs, nch = n_kv_heads // team, chunks // team
     P = (np.asarray(seq_lens, dtype=np.int64) + page_size - 1) // page_size
+    Pr = np.repeat(P[:, None], hs, axis=1)
     if num_splits == 1:
-        return int((P > 0).sum()) * n_kv_heads
-    tp = int(P.sum()) * n_kv_heads
-    qp = max(-(-tp // chunks), -(-int(P.max()) // (num_splits - 1)), 1)
-    G = (np.concatenate([[0], np.cumsum(P)[:-1]])[:, None] * n_kv_heads
-         + np.arange(n_kv_heads)[None, :] * P[:, None])
-    Pr = np.repeat(P[:, None], n_kv_heads, axis=1)
-    n = np.where(Pr > 0, (G + Pr - 1) // qp - G // qp + 1, 0)
-    return int(n.sum())
+        n = (Pr > 0).astype(np.int64)
+    else:
+        tp = int(P.sum()) * hs
+        qp = max(-(-tp // nch), -(-int(P.max()) // (num_splits - 1)), 1)
+        G = np.concatenate([[0], np.cumsum(P)[:-1]])[:, None] * hs + np.arange(hs)[None, :] * P[:, None]
+        n = np.where(Pr > 0, (G + Pr - 1) // qp - G // qp + 1, 0)
+    return np.repeat(n, team, axis=1)
+
+
+def split_segments(seq_lens, page_size, n_kv_heads, num_splits):
+    """Number of non-empty (request, kv head, split) partials the plan writes."""
+    return int(row_splits(seq_lens, page_size, n_kv_heads, num_splits).sum())
 
 
 def attn_bytes(seq_lens, n_kv_heads, head_dim, batch, n_heads, num_splits, page_size):

@@ -125,7 +125,7 @@ pd_status paged_decode_layout(const pd_handle* h, pd_layout* out);
 /* Resolves the split count S for a batch: requested > 0 is honoured (it must be
  * <= max_splits); requested == 0 picks S = 1 + ceil(4096 / (batch*n_kv_heads)),
  * capped at max_splits and max_pages_per_req (at least 2), so that the split
- * plan below can give all 2048 chunks the same number of pages.
+ * plan below can give all chunks the same number of pages.
  * Pass the same S to paged_decode_attn and paged_decode_merge. */
 pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t requested,
                                   int32_t* num_splits);
@@ -148,17 +148,20 @@ pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* 
  *   d_k_store  bf16 [n_layers, num_slots, n_kv_heads, head_dim] (base of the
  *   d_v_store  whole store; the library adds the 64-bit offset of `layer`)
  *   scale      softmax scale applied to q.k (float32)
- * Split plan (S = num_splits, P_b = ceil(L_b / page_size)): the rows
- * (request b, kv head g) are laid end to end, request-major, each as its P_b
- * pages.  S = 1: each row is one split.  S >= 2: the page sequence is cut
- * into chunks of Qp = max(ceil(TP / 2048), ceil(P_max / (S - 1)), 1) pages
- * (TP = n_kv_heads * sum P_b, P_max = max P_b), and split j of row (b, g) is
- * the row's intersection with the j-th chunk that touches it -- a contiguous,
- * page-aligned token range; a row never has more than S splits.  For every
+ * Split plan (S = num_splits, P_b = ceil(L_b / page_size)): the kv heads
+ * form bundles of T = gcd(n_kv_heads, 4) consecutive heads, and the bundle
+ * rows (request b, bundle gs) are laid end to end, request-major, each as its
+ * P_b pages.  S = 1: each row is one split.  S >= 2: the page sequence is cut
+ * into chunks of Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1) pages
+ * (C = 2048 / T, TP = (n_kv_heads / T) * sum P_b, P_max = max P_b), and split
+ * j of row (b, g) is the intersection of bundle row (b, g / T) with the j-th
+ * chunk that touches it -- a contiguous, page-aligned token range; a row
+ * never has more than S splits.  For every
  * query head h of kv head g, o_part[b,h,j,:] and ml_part[b,h,j,:] describe
  * split j; splits past a row's last one are empty: ml = (-inf, -inf) and
  * o_part is left unspecified.  Reads kv_indptr / kv_indices / page_indptr
- * from the last bind.  One launch of 512 workgroups (2048 waves). */
+ * from the last bind.  One launch of 512 workgroups (2048 waves; the T waves
+ * of a team read the T heads of one bundle over the same chunk). */
 pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
                             const void* d_q, const void* d_k_store, const void* d_v_store,
                             float scale, hipStream_t stream);

@@ -24,10 +24,12 @@ from .paged_attention import (  # noqa: F401
     bind_steady,
     decode_attention,
     gather_rows,
+    kv_team,
     kv_indices,
     kv_indptr,
     merge_splits,
     SPLIT_CHUNKS,
+    TEAM_MAX,
     chunk_pages,
     split_partials,
     split_plan,

@@ -153,45 +153,59 @@ def decode_attention(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale
 # decode_o_part / decode_ml_part and the split partial buffers).
 # --------------------------------------------------------------------------
 
-SPLIT_CHUNKS = 2048  # the page sequence is cut into at most this many chunks
+SPLIT_CHUNKS = 2048  # waves of the attention launch
+TEAM_MAX = 4         # at most this many kv heads share one page stream
+
+
+def kv_team(n_kv_heads):
+    """Heads per bundle: gcd(n_kv_heads, 4)."""
+    return math.gcd(int(n_kv_heads), TEAM_MAX)
 
 
 def _pages(seq_lens, page_size):
     return [-(-int(x) // page_size) for x in np.asarray(seq_lens).reshape(-1)]
 
 
-def chunk_pages(seq_lens, page_size, n_kv_heads, S, n_chunks=SPLIT_CHUNKS):
-    """Qp for S >= 2: max(ceil(TP / n_chunks), ceil(P_max / (S - 1)), 1)."""
+def chunk_pages(seq_lens, page_size, n_kv_heads, S, n_chunks=None, team=None):
+    """Qp for S >= 2: max(ceil(TP / C), ceil(P_max / (S - 1)), 1), where the
+    bundle rows hold TP = (n_kv_heads / team) * sum P pages and C = 2048 / team."""
+    team = kv_team(n_kv_heads) if team is None else int(team)
+    n_chunks = SPLIT_CHUNKS // team if n_chunks is None else int(n_chunks)
     P = _pages(seq_lens, page_size)
-    tp = n_kv_heads * sum(P)
+    tp = (n_kv_heads // team) * sum(P)
     p_max = max(P + [0])
     return max(-(-tp // n_chunks), -(-p_max // (int(S) - 1)), 1)
 
 
-def split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks=SPLIT_CHUNKS):
+def split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks=None, team=None):
     """Token ranges of the splits: plan[b][g] = [(lo, hi), ...] indexed by j.
 
-    Walks the rows in order, page by page, and starts a new split whenever the
-    chunk index of the global page changes (S >= 2) or a row begins.
+    The kv heads form bundles of ``team`` heads (gs = g // team); the bundle
+    rows (b, gs) are walked in order, page by page, and a new split starts
+    whenever the chunk index of the global page changes (S >= 2) or a row
+    begins.  Every head of a bundle gets its bundle row's splits.
     """
+    team = kv_team(n_kv_heads) if team is None else int(team)
+    assert n_kv_heads % team == 0
+    hs = n_kv_heads // team
     L = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
     P = _pages(L, page_size)
-    plan = [[[] for _ in range(n_kv_heads)] for _ in L]
-    qp = None if int(S) == 1 else chunk_pages(L, page_size, n_kv_heads, S, n_chunks)
+    qp = None if int(S) == 1 else chunk_pages(L, page_size, n_kv_heads, S, n_chunks, team)
+    bundle = [[[] for _ in range(hs)] for _ in L]
     gp = 0  # global page index of the current page
     for b, lb in enumerate(L):
-        for g in range(n_kv_heads):
+        for gs in range(hs):
             cur = None  # (chunk id, first local page)
             for lp in range(P[b]):
                 k = 0 if qp is None else gp // qp
                 if cur is None or k != cur[0]:
                     if cur is not None:
-                        plan[b][g].append((cur[1] * page_size, min(lp * page_size, lb)))
+                        bundle[b][gs].append((cur[1] * page_size, min(lp * page_size, lb)))
                     cur = (k, lp)
                 gp += 1
             if cur is not None:
-                plan[b][g].append((cur[1] * page_size, lb))
-    return plan
+                bundle[b][gs].append((cur[1] * page_size, lb))
+    return [[list(bundle[b][g // team]) for g in range(n_kv_heads)] for b in range(len(L))]
 
 
 def split_partials(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale,

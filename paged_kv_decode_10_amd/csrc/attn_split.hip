@@ -5,18 +5,23 @@
 // preallocated decode_o_part / decode_ml_part buffers, and a merge produces
 // decode_out.  The partition and everything below are this kernel's own design.
 //
-// Work plan.  The rows (request b, kv head g) are laid end to end, request
-// major, each as its P_b = ceil(L_b / page_size) pages.  With S >= 2 splits
-// the page sequence is cut into chunks of
-//     Qp = max(ceil(TP / 2048), ceil(P_max / (S - 1)), 1)
-// pages (TP = total pages of all rows), and wave w of the launch processes
-// chunk w: a contiguous run of pages that may end one row and start the next.
-// Split j of a row is its intersection with the j-th chunk touching it, so a
-// row has at most S splits and every wave carries the same number of pages:
-// the work is balanced across waves, CUs and XCDs whatever the length mix.
-// With S = 1 rows are not split: wave w takes rows w, w + 2048, ...
+// Work plan.  The kv heads are bundled in teams of T = gcd(n_kv_heads, 4)
+// heads, and the launch's 2048 waves in teams of T waves (within one
+// workgroup).  The bundle rows (request b, bundle gs) are laid end to end,
+// request major, each as its P_b = ceil(L_b / page_size) pages.  With S >= 2
+// splits the page sequence is cut into chunks of
+//     Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1)
+// pages (C = 2048 / T chunks, TP = total pages of all bundle rows), and team
+// t processes chunk t: a contiguous run of pages that may end one bundle row
+// and start the next; wave i of the team reads kv head T*gs + i of those
+// pages, so a team reads T contiguous head rows of every token together.
+// Split j of a row (b, g) is its bundle row's intersection with the j-th
+// chunk touching it, so a row has at most S splits and every wave carries
+// the same number of pages: the work is balanced across waves, CUs and XCDs
+// whatever the length mix.  With S = 1 rows are not split: team t takes
+// bundle rows t, t + C, ...
 //
-// Per wave (4 independent waves per workgroup, no LDS, no barriers), the
+// Per wave (no LDS, no barriers: the waves of a team share only the plan), the
 // pages are consumed as 16-token units (a page, or a 16-token piece of a
 // larger page) in a software pipeline that crosses row boundaries: the slots
 // of unit n+4 are requested while unit n is computed, and its K, V and q rows
@@ -88,19 +93,19 @@ struct Unit {
   int last;    // last unit of a row segment: write the split
   int row_end; // the segment ends the row: splits after it are empty
   int ntok;    // valid tokens in the unit (lanes c < ntok)
-  int b, g, j;
+  int b, g, j;   // g: the wave's kv head
   int32_t slot;  // per lane: slot of token c (a real row of the request)
 };
 
 // Walks this wave's pages in order and describes one unit per call.
 struct Producer {
-  // launch constants
-  int B, Hkv, ps, ut, upp, S, w, row_mode;
+  // launch constants (Hs = bundle rows per request, nch = chunks, w = team)
+  int B, Hs, ps, ut, upp, S, w, row_mode, nch, team, member;
   int64_t Qp, p1;
   const int32_t* kv_indptr;
   const int32_t* page_indptr;
   const int32_t* kv_indices;
-  // current row segment
+  // current row segment (g = bundle index)
   int done, b, g, j;
   int32_t start, L, P;
   int64_t G;      // global page index of the row's first page
@@ -116,16 +121,16 @@ struct Producer {
     P = pages_of(b);
   }
 
-  // Row mode (S = 1): rows w, w + 2048, ...; chunk mode: rows after (b, g).
+  // Row mode (S = 1): bundle rows w, w + nch, ...; chunk mode: rows after (b, g).
   __device__ void next_segment() {
     if (row_mode) {
-      int r = b * Hkv + g + kSplitChunks;
+      int r = b * Hs + g + nch;
       for (;;) {
-        if (r >= B * Hkv) { done = 1; return; }
-        b = r / Hkv;
-        g = r % Hkv;
+        if (r >= B * Hs) { done = 1; return; }
+        b = r / Hs;
+        g = r % Hs;
         if (pages_of(b) > 0) break;
-        r += kSplitChunks;
+        r += nch;
       }
       open_row();
       lp = 0; piece = 0; lp_end = P; j = 0; seg_first = 1;
@@ -135,13 +140,13 @@ struct Producer {
     // Candidate next row; b and g only change once it is known to exist, so
     // the (masked) loads issued after the end still address real rows.
     int nb = b, ng = g + 1;
-    if (ng == Hkv) {
+    if (ng == Hs) {
       ng = 0;
       ++nb;
       while (nb < B && pages_of(nb) == 0) ++nb;
       if (nb >= B) { done = 1; return; }
     }
-    const int64_t nG = (int64_t)Hkv * page_indptr[nb] + (int64_t)ng * pages_of(nb);
+    const int64_t nG = (int64_t)Hs * page_indptr[nb] + (int64_t)ng * pages_of(nb);
     if (nG >= p1) { done = 1; return; }
     b = nb;
     g = ng;
@@ -156,7 +161,7 @@ struct Producer {
   __device__ Unit next(int c) {
     Unit u;
     u.valid = !done;
-    u.b = b; u.g = g; u.j = j;
+    u.b = b; u.g = g * team + member; u.j = j;
     u.first = seg_first;
     const int tok_lo = lp * ps + piece * ut;
     const int tok_hi = min(lp * ps + min((piece + 1) * ut, ps), L);
@@ -245,17 +250,24 @@ __global__ void __launch_bounds__(kThreads, 2)
 split_attn_kernel(AttnArgs a) {
   constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
   const int lane = threadIdx.x & 63;
-  // Chunk index of this wave (wave-uniform, so the plan lives in SGPRs).
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int wave = threadIdx.x >> 6;
+  // Wave index, team (= chunk) index and head within the team: wave-uniform,
+  // so the plan lives in SGPRs.
+  const int T = a.team;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
+  const int tm = __builtin_amdgcn_readfirstlane(blockIdx.x * (kWaves / T) + wave / T);
+  const int member = __builtin_amdgcn_readfirstlane(wave % T);
   const int r = lane >> 4, c = lane & 15;
   const int B = a.batch, Hkv = a.n_kv_heads, S = a.num_splits, H = a.n_heads;
+  const int Hs = Hkv / T, nch = kSplitChunks / T;
   PD_STAMP(0, wall_clock64());
 
   // ---- this wave's first row segment ----
   // All plan inputs are fetched in one round trip: the meta words, and (for
   // the first 64 requests) page_indptr and kv_indptr, held one per lane.
   Producer pr;
-  pr.B = B; pr.Hkv = Hkv; pr.ps = a.page_size; pr.S = S; pr.w = w;
+  pr.B = B; pr.Hs = Hs; pr.ps = a.page_size; pr.S = S; pr.w = tm;
+  pr.nch = nch; pr.team = T; pr.member = member;
   pr.ut = a.page_size < 16 ? a.page_size : 16;
   pr.upp = (a.page_size + pr.ut - 1) / pr.ut;
   pr.kv_indptr = a.kv_indptr; pr.page_indptr = a.page_indptr; pr.kv_indices = a.kv_indices;
@@ -267,45 +279,45 @@ split_attn_kernel(AttnArgs a) {
   const int32_t ki_lane = a.kv_indptr[i_lane];
   const int32_t total_pages = a.meta[kMetaTotalPages];
   const int32_t max_pages = a.meta[kMetaMaxPages];
-  const int64_t TP = (int64_t)Hkv * total_pages;
+  const int64_t TP = (int64_t)Hs * total_pages;
   // page_indptr / kv_indptr of request bb (from the lane registers when bb < 64)
   auto pi_of = [&](int bb) { return bb < 64 ? __shfl(pi_lane, bb, 64) : a.page_indptr[bb]; };
   auto ki_of = [&](int bb) { return bb < 64 ? __shfl(ki_lane, bb, 64) : a.kv_indptr[bb]; };
   bool active = true;
   if (row_mode) {
     pr.Qp = 1; pr.p1 = 0;
-    int rr = w;  // first non-empty row among w, w + 2048, ...
+    int rr = tm;  // first non-empty bundle row among tm, tm + nch, ...
     for (;;) {
-      if (rr >= B * Hkv) { active = false; break; }
-      const int bb = rr / Hkv;
+      if (rr >= B * Hs) { active = false; break; }
+      const int bb = rr / Hs;
       if (pi_of(bb + 1) - pi_of(bb) > 0) break;
-      rr += kSplitChunks;
+      rr += nch;
     }
     if (active) {
-      pr.b = __builtin_amdgcn_readfirstlane(rr / Hkv);
-      pr.g = __builtin_amdgcn_readfirstlane(rr % Hkv);
+      pr.b = __builtin_amdgcn_readfirstlane(rr / Hs);
+      pr.g = __builtin_amdgcn_readfirstlane(rr % Hs);
       pr.start = __builtin_amdgcn_readfirstlane(ki_of(pr.b));
       pr.L = __builtin_amdgcn_readfirstlane(ki_of(pr.b + 1)) - pr.start;
       pr.P = __builtin_amdgcn_readfirstlane(pi_of(pr.b + 1) - pi_of(pr.b));
       pr.lp = 0; pr.piece = 0; pr.lp_end = pr.P; pr.j = 0; pr.seg_first = 1;
     }
   } else {
-    int64_t qp = (TP + kSplitChunks - 1) / kSplitChunks;
+    int64_t qp = (TP + nch - 1) / nch;
     const int64_t qs = (max_pages + S - 2) / (S - 1);
     qp = qp > qs ? qp : qs;
     qp = qp < 1 ? 1 : qp;
-    const int64_t p0 = (int64_t)w * qp;
+    const int64_t p0 = (int64_t)tm * qp;
     if (p0 >= TP) {
       active = false;
     } else {
       pr.Qp = qp;
       pr.p1 = p0 + qp < TP ? p0 + qp : TP;
       // Request holding global page p0: the number of entries of
-      // Hkv * page_indptr[0..B] that are <= p0, minus one.
-      int cnt = __popcll(__builtin_amdgcn_ballot_w64(lane <= B && (int64_t)Hkv * pi_lane <= p0));
+      // Hs * page_indptr[0..B] that are <= p0, minus one.
+      int cnt = __popcll(__builtin_amdgcn_ballot_w64(lane <= B && (int64_t)Hs * pi_lane <= p0));
       for (int i0 = 64; i0 <= B; i0 += 64) {
         const int i = i0 + lane;
-        const bool le = i <= B && (int64_t)Hkv * a.page_indptr[i] <= p0;
+        const bool le = i <= B && (int64_t)Hs * a.page_indptr[i] <= p0;
         cnt += __popcll(__builtin_amdgcn_ballot_w64(le));
       }
       pr.b = cnt - 1;
@@ -313,13 +325,13 @@ split_attn_kernel(AttnArgs a) {
       pr.P = __builtin_amdgcn_readfirstlane(pi_of(pr.b + 1)) - pib;
       pr.start = __builtin_amdgcn_readfirstlane(ki_of(pr.b));
       pr.L = __builtin_amdgcn_readfirstlane(ki_of(pr.b + 1)) - pr.start;
-      const int64_t off = p0 - (int64_t)Hkv * pib;
+      const int64_t off = p0 - (int64_t)Hs * pib;
       pr.g = (int)(off / pr.P);
-      pr.G = (int64_t)Hkv * pib + (int64_t)pr.g * pr.P;
+      pr.G = (int64_t)Hs * pib + (int64_t)pr.g * pr.P;
       pr.lp = (int)(off % pr.P);
       pr.piece = 0;
       pr.lp_end = (int)min((int64_t)pr.P, pr.p1 - pr.G);
-      pr.j = (int)(w - pr.G / qp);
+      pr.j = (int)(tm - pr.G / qp);
       pr.seg_first = 1;
     }
   }

@@ -198,6 +198,7 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
   a.group = c.n_heads / c.n_kv_heads;
   a.page_size = c.page_size;
   a.num_splits = num_splits;
+  a.team = pd::kv_team(c.n_kv_heads);
   a.max_splits = c.max_splits;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   a.q = static_cast<const uint16_t*>(d_q);

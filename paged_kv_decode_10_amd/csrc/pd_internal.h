@@ -16,9 +16,16 @@ enum MetaWord : int {
   kMetaTotalPages = 2,   // sum over requests of ceil(L_b / page_size)
 };
 
-// The split plan cuts the page sequence of all (request, kv head) rows into
-// at most this many equal chunks; the attention launches one wave per chunk.
+// The attention launches this many waves.  They work in teams of
+// kv_team(n_kv_heads) waves; a team walks one chunk of the page sequence and
+// each of its waves reads one kv head of those pages.
 constexpr int kSplitChunks = 2048;
+constexpr int kTeamMax = 4;  // waves per workgroup
+
+// Waves per team = kv heads per bundle: gcd(n_kv_heads, 4).
+inline __host__ __device__ int kv_team(int n_kv_heads) {
+  return (n_kv_heads % 4 == 0) ? 4 : (n_kv_heads % 2 == 0) ? 2 : 1;
+}
 
 struct BindArgs {
   int32_t batch;
@@ -44,6 +51,7 @@ struct AttnArgs {
   int32_t group;              // n_heads / n_kv_heads
   int32_t page_size;
   int32_t num_splits;         // S used for this launch
+  int32_t team;               // kv_team(n_kv_heads)
   int32_t max_splits;         // stride of the partial buffers
   float scale_log2;           // scale * log2(e)
   const uint16_t* q;          // bf16 [batch, n_heads, D]

@@ -238,34 +238,46 @@ def test_page_permutation_invariance_bit_exact():
 
 # --------------------------------------------------------------- splits ----
 
-def test_split_plan_golden():
-    g = _load("split_example.json")
+@pytest.mark.parametrize("name", ["split_example.json", "split_example_team2.json"])
+def test_split_plan_golden(name):
+    g = _load(name)
     for S, want in g["plans"].items():
-        plan = oracle.split_plan(g["seq_lens"], g["page_size"], g["n_kv_heads"], int(S))
+        plan = oracle.split_plan(g["seq_lens"], g["page_size"], g["n_kv_heads"], int(S), n_chunks=g["n_chunks"],
+                                 team=g["team"])
         got = [[[list(r) for r in plan[b][h]] for h in range(g["n_kv_heads"])] for b in range(2)]
         assert got == want, S
+    if g["team"] == oracle.kv_team(g["n_kv_heads"]):  # the defaults are the launch's
+        for S, want in g["plans"].items():
+            plan = oracle.split_plan(g["seq_lens"], g["page_size"], g["n_kv_heads"], int(S))
+            assert [[[list(r) for r in plan[b][h]] for h in range(2)] for b in range(2)] == want
 
 
-def _brute_plan(L, ps, hkv, S, n_chunks):
-    """Same rule, computed another way: chunk id of every (row, page) pair, then
-    group each row's pages by chunk id."""
+def test_kv_team():
+    assert [oracle.kv_team(h) for h in (1, 2, 3, 4, 6, 8, 12, 16, 5)] == [1, 2, 1, 4, 2, 4, 4, 4, 1]
+
+
+def _brute_plan(L, ps, hkv, S, n_chunks, team):
+    """Same rule, computed another way: chunk id of every (bundle row, page)
+    pair, then group each bundle row's pages by chunk id; every head of a
+    bundle takes its bundle's ranges."""
     P = [-(-x // ps) for x in L]
-    rows = [(b, g) for b in range(len(L)) for g in range(hkv)]
-    flat = [(b, g, lp) for (b, g) in rows for lp in range(P[b])]
+    rows = [(b, gs) for b in range(len(L)) for gs in range(hkv // team)]
+    flat = [(b, gs, lp) for (b, gs) in rows for lp in range(P[b])]
     if S == 1:
-        cid = [rows.index((b, g)) for (b, g, lp) in flat]
+        cid = [rows.index((b, gs)) for (b, gs, lp) in flat]
     else:
         tp, pm = len(flat), max(P + [0])
         qp = max(math.ceil(tp / n_chunks), math.ceil(pm / (S - 1)), 1)
         cid = [i // qp for i in range(len(flat))]
     out = {}
-    for (b, g, lp), k in zip(flat, cid):
-        out.setdefault((b, g), {}).setdefault(k, []).append(lp)
+    for (b, gs, lp), k in zip(flat, cid):
+        out.setdefault((b, gs), {}).setdefault(k, []).append(lp)
     plan = [[[] for _ in range(hkv)] for _ in L]
-    for (b, g), groups in out.items():
+    for (b, gs), groups in out.items():
         for k in sorted(groups):
             pages = groups[k]
-            plan[b][g].append((pages[0] * ps, min((pages[-1] + 1) * ps, L[b])))
+            for g in range(gs * team, (gs + 1) * team):
+                plan[b][g].append((pages[0] * ps, min((pages[-1] + 1) * ps, L[b])))
     return plan
 
 
@@ -274,18 +286,19 @@ def test_split_plan_brute_force(seed):
     rng = np.random.default_rng(seed)
     ps = int(rng.choice([1, 3, 16]))
     L = [int(x) for x in rng.integers(0, 90, size=int(rng.integers(1, 6)))]
-    hkv = int(rng.integers(1, 4))
-    for S in (1, 2, 3, 5, 9):
-        for nc in (2, 7, 2048):
-            got = oracle.split_plan(L, ps, hkv, S, n_chunks=nc)
-            assert got == _brute_plan(L, ps, hkv, S, nc), (S, nc)
-            for b in range(len(L)):
-                for g in range(hkv):
-                    rr = got[b][g]
-                    assert len(rr) <= S
-                    assert sum(hi - lo for lo, hi in rr) == L[b]
-                    assert all(lo % ps == 0 and lo < hi for lo, hi in rr)
-                    assert all(rr[i][1] == rr[i + 1][0] for i in range(len(rr) - 1))
+    hkv = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    for team in sorted({1, oracle.kv_team(hkv)}):
+        for S in (1, 2, 3, 5, 9):
+            for nc in (2, 7, 2048 // team):
+                got = oracle.split_plan(L, ps, hkv, S, n_chunks=nc, team=team)
+                assert got == _brute_plan(L, ps, hkv, S, nc, team), (S, nc, team)
+                for b in range(len(L)):
+                    for g in range(hkv):
+                        rr = got[b][g]
+                        assert len(rr) <= S
+                        assert sum(hi - lo for lo, hi in rr) == L[b]
+                        assert all(lo % ps == 0 and lo < hi for lo, hi in rr)
+                        assert all(rr[i][1] == rr[i + 1][0] for i in range(len(rr) - 1))
 
 
 @pytest.mark.parametrize("S", [1, 2, 4, 7, 32])
