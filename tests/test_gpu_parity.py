@@ -194,6 +194,32 @@ def test_split_count_consistency_and_determinism():
         assert torch.all(d <= 2e-2 + 2e-2 * outs[1].double().abs()).item()
 
 
+def test_rebind_with_other_lengths():
+    """A new bind with other lengths (same batch and split count) changes the
+    plan; rebinding the first lengths reproduces the first result bit for bit."""
+    say("[plan] rebind with other lengths")
+    w = workloads.make_custom("plan", seed=16, n_layers=1, seq_lens=[700, 40, 2500, 1, 333], n_heads=16,
+                              n_kv_heads=4, head_dim=128, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    S = 9
+    _bind(ws, w, dev)
+    first = run_layer(ws, w, dev, 0, S).clone()
+    cached = run_layer(ws, w, dev, 0, S).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), cached.view(torch.int16))
+    L2 = (w.seq_lens // 3).numpy()
+    dev.seq_lens.copy_(torch.from_numpy(L2).to(torch.int32))
+    _bind(ws, w, dev)
+    check_layer(ws, w, dev, 0, S, seq_lens_host=L2)
+    check_layer(ws, w, dev, 0, S, seq_lens_host=L2)
+    dev.seq_lens.copy_(w.seq_lens)
+    _bind(ws, w, dev)
+    again = run_layer(ws, w, dev, 0, S)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
 # --------------------------------------------------------- larger configs ----
 
 def test_b1_parity():
