@@ -19,6 +19,8 @@ examples); no function is "parity unpinned".
 """
 from .paged_attention import (  # noqa: F401
     NEG_INF,
+    append_kv,
+    append_slots,
     attention_rows,
     bind_full,
     bind_steady,

@@ -16,14 +16,19 @@ bullets and print no formulas):
     there is no mask ([CA] bullets dropping decode_mask / page_table).
   * Softmax is natural-base; ``scale`` is the float32 value the kernel gets.
   * Split partition (the pages fix no rule; any partition yields the same
-    merged output).  The rows (request b, kv head g) are laid end to end,
-    request-major, each as its P_b pages.  With S = 1 every non-empty row is
-    one split.  With S >= 2 that page sequence is cut into chunks of
-    Qp = max(ceil(TP / 2048), ceil(P_max / (S - 1)), 1) pages (TP = total
-    pages of all rows); split j of a row is its intersection with the j-th
-    chunk that touches it.  A row then never has more than S splits, and
-    every chunk holds the same number of pages.  Splits past a row's last
-    chunk are empty.
+    merged output).  The kv heads form bundles of T = gcd(Hkv, 4); the
+    bundle rows (request b, bundle gs) are laid end to end, request-major,
+    each as its P_b pages.  With S = 1 every non-empty row is one split.
+    With S >= 2 that page sequence is cut into chunks of
+    Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1) pages (C = 2048 / T,
+    TP = total pages of all bundle rows); split j of row (b, g) is the
+    intersection of bundle row (b, g // T) with the j-th chunk that touches
+    it.  A row then never has more than S splits, and every chunk holds the
+    same number of pages.  Splits past a row's last chunk are empty.
+  * Per-layer KV append ([CA] bullets on the single-index write
+    buffer[layer_id, loc] and on moving the slot bookkeeping into
+    bind_tasks): the new token is already counted in seq_lens, so it is
+    position L_b - 1 and its K/V rows go to that position's slot.
   * Per-split outputs ([WS] bullet on decode_o_part / decode_ml_part): o_j is
     normalised by its own softmax sum; the (m, log-sum) pair is
     m_j = max score, ln l_j with l_j = sum exp(s - m_j), so lse_j = m_j + ln l_j.
@@ -91,6 +96,33 @@ def bind_steady(seq_lens, position_ids):
 def bind_full(seq_lens, req_to_page, page_size):
     """(kv_indptr, kv_indices) for the given lengths and page table."""
     return kv_indptr(seq_lens), kv_indices(seq_lens, req_to_page, page_size)
+
+
+# --------------------------------------------------------------------------
+# Per-layer KV append ([CA] bullets on the buffer[layer_id, loc] write).
+# --------------------------------------------------------------------------
+
+def append_slots(seq_lens, req_to_page, page_size: int) -> np.ndarray:
+    """Slot of each request's newest token, position L_b - 1, or -1 when the
+    request has no tokens: req_to_page[b][t // ps] * ps + t % ps, t = L_b - 1."""
+    L = np.asarray(seq_lens).reshape(-1).astype(np.int64)
+    table = np.asarray(req_to_page).astype(np.int64)
+    out = np.full(len(L), -1, dtype=np.int64)
+    for b in range(len(L)):
+        if L[b] > 0:
+            t = L[b] - 1
+            out[b] = table[b, t // page_size] * page_size + t % page_size
+    return out
+
+
+def append_kv(store_layer, new_rows, slots):
+    """A copy of one layer of a store ([num_slots, Hkv, D]) with new_rows[b]
+    ([Hkv, D]) written at slots[b] for every slots[b] >= 0 (a bit copy)."""
+    out = store_layer.clone()
+    for b, slot in enumerate(np.asarray(slots).reshape(-1)):
+        if slot >= 0:
+            out[int(slot)] = new_rows[b]
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -66,6 +66,46 @@ def test_bind_golden():
     ip2, ix2 = oracle.bind_full(sl, np.array(g["req_to_page"]), g["page_size"])
     assert ip2.tolist() == g["steady"]["kv_indptr"]
     assert ix2.tolist() == g["steady"]["kv_indices"]
+    assert oracle.append_slots(g["seq_lens"], np.array(g["req_to_page"]), g["page_size"]).tolist() == \
+        g["append_slots"]
+    assert oracle.append_slots(sl, np.array(g["req_to_page"]), g["page_size"]).tolist() == \
+        g["steady"]["append_slots"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_append_slots_brute_force(seed):
+    """The newest token's slot, found another way: walk the request's pages in
+    order, listing their slots, and take entry L_b - 1."""
+    rng = np.random.default_rng(100 + seed)
+    ps = int(rng.choice([1, 3, 16]))
+    lens = [int(x) for x in rng.integers(0, 50, size=int(rng.integers(1, 7)))]
+    lens[0] = 0
+    pages = [-(-x // ps) for x in lens]
+    perm = rng.permutation(sum(pages) + 3)
+    width = max(pages + [1])
+    table = np.full((len(lens), width), -1, dtype=np.int64)
+    off = 0
+    for b, p in enumerate(pages):
+        table[b, :p] = perm[off:off + p]
+        off += p
+    got = oracle.append_slots(lens, table, ps)
+    for b, lb in enumerate(lens):
+        listed = [int(pg) * ps + o for pg in table[b, :pages[b]] for o in range(ps)]
+        assert got[b] == (listed[lb - 1] if lb else -1)
+
+
+def test_append_kv_writes_only_the_new_rows():
+    g = torch.Generator().manual_seed(7)
+    store = torch.randn((40, 3, 8), generator=g).to(torch.bfloat16)
+    new = torch.randn((4, 3, 8), generator=g).to(torch.bfloat16)
+    slots = np.array([5, -1, 39, 0])
+    out = oracle.append_kv(store, new, slots)
+    assert store.shape == out.shape and out.data_ptr() != store.data_ptr()
+    for b, s in enumerate(slots):
+        if s >= 0:
+            assert torch.equal(out[s].view(torch.int16), new[b].view(torch.int16))
+    keep = [i for i in range(40) if i not in (5, 39, 0)]
+    assert torch.equal(out[keep].view(torch.int16), store[keep].view(torch.int16))
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
