@@ -126,6 +126,96 @@ def cpu_baseline(w, budget_s: float, num_splits: int):
                       f"BLAS threads {blas}; numpy {np.__version__}"}
 
 
+def config_sweep(names, reps: int, oracle_budget: float):
+    """Per-config attention and merge timings with the caches flushed.
+
+    For each workload: one bind, then ``reps`` iterations of [1 GiB
+    flush-write, attn, merge] with HIP events around the attention and the
+    merge separately (on the launch stream).  Reports median / p10 / p90 and
+    the KV-only and all-algorithmic rates at the median.  With
+    ``oracle_budget`` > 0 the oracle is timed on the same inputs, one
+    (request, kv head) pair at a time, for at most about that many seconds
+    per config.
+    """
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_decode_10_amd import PD_BIND_FULL, Config, PagedDecode
+
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    rows = []
+    for name in names:
+        t0 = time.perf_counter()
+        w = workloads.make(name)
+        B, H, Hkv, D = w.batch, w.n_heads, w.n_kv_heads, w.head_dim
+        cfg = Config(n_layers=w.n_layers, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size,
+                     max_batch=B, max_splits=256, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
+                     max_total_tokens=int(w.seq_lens.sum()))
+        ws = PagedDecode(cfg)
+        seq, pos, tab = w.seq_lens.cuda(), w.position_ids.cuda(), w.req_to_page.cuda()
+        q, kst, vst = w.q.cuda(), w.k_store.cuda(), w.v_store.cuda()
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+        S = ws.num_splits(B)
+        ws.bind(B, PD_BIND_FULL, seq, pos, tab)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ta, tm = [], []
+        for r in range(reps + 2):
+            flush.fill_(r)
+            ev[0].record()
+            ws.attn(B, 0, S, q[0], kst, vst, w.scale)
+            ev[1].record()
+            ws.merge(B, S, out)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ta.append(ev[0].elapsed_time(ev[1]) * 1e3)
+                tm.append(ev[1].elapsed_time(ev[2]) * 1e3)
+        assert ws.read_error() == 0 and torch.isfinite(out.float()).all()
+        L = w.seq_lens.to(torch.int64)
+        kv, alg = attn_bytes(L, Hkv, D, B, H, S, w.page_size)
+        pa = np.percentile(ta, [50, 10, 90])
+        pm = np.percentile(tm, [50, 10, 90])
+        row = {"workload": name, "batch": B, "n_heads": H, "n_kv_heads": Hkv, "head_dim": D,
+               "sum_seq_len": int(L.sum()), "num_splits": S,
+               "attn_us": {"median": round(pa[0], 2), "p10": round(pa[1], 2), "p90": round(pa[2], 2)},
+               "merge_us": {"median": round(pm[0], 2), "p10": round(pm[1], 2), "p90": round(pm[2], 2)},
+               "kv_bytes": kv, "algorithmic_bytes": alg,
+               "kv_gbs": round(kv / pa[0] / 1e3, 1), "kv_pct_of_peak": round(100 * kv / pa[0] / 1e3 / HBM_PEAK_GBS, 1),
+               "alg_gbs": round(alg / pa[0] / 1e3, 1),
+               "kv_gbs_attn_plus_merge": round(kv / (pa[0] + pm[0]) / 1e3, 1),
+               "us_per_layer_attn_plus_merge": round(pa[0] + pm[0], 2)}
+        if oracle_budget > 0:
+            row["oracle"] = oracle_time(w, oracle_budget)
+        rows.append(row)
+        log(f"[configs] {name}: B={B} sum(L)={int(L.sum())} S={S} attn {pa[0]:.2f} us (p10 {pa[1]:.2f}, "
+            f"p90 {pa[2]:.2f}) -> {row['kv_gbs']:.0f} GB/s KV ({row['kv_pct_of_peak']}%), merge {pm[0]:.2f} us; "
+            f"{time.perf_counter() - t0:.1f} s")
+        del ws, q, kst, vst
+        torch.cuda.empty_cache()
+    return rows
+
+
+def oracle_time(w, budget_s: float):
+    """The oracle's decode attention on (request, kv head) pairs of the same
+    inputs until about budget_s, scaled to KV bytes per second."""
+    import oracle
+
+    L = w.seq_lens.numpy()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    pairs = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    done, kv = 0, 0
+    t0 = time.perf_counter()
+    for pr in pairs:
+        oracle.decode_attention(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale, w.n_kv_heads, pairs=[pr])
+        done += 1
+        kv += int(L[pr[0]]) * w.head_dim * 4
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"pairs": done, "of": len(pairs), "seconds": round(dt, 2), "kv_gbs": round(kv / dt / 1e9, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +225,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--configs", default="",
+                    help="instead of the step: comma-separated workloads (e.g. tiny,b1,b16,long,sweep1,...,sweep32) "
+                         "timed one launch at a time with the caches flushed; prints one JSON line")
+    ap.add_argument("--config-reps", type=int, default=20)
+    ap.add_argument("--oracle-budget", type=float, default=0.0,
+                    help="with --configs: seconds of oracle timing per config (0 = none)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -152,6 +248,12 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 2
+    if args.configs:
+        rows = config_sweep([x for x in args.configs.split(",") if x], args.config_reps, args.oracle_budget)
+        print(json.dumps({"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "data": "synthetic", "dtype": "bf16",
+                          "timing": "HIP events per launch, 1 GiB flush-write before each iteration",
+                          "configs": rows}), flush=True)
+        return 0
     K, W = args.steps, args.warmup
     growth = max(256, K + W + 8)
     t0 = time.perf_counter()

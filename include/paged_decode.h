@@ -166,6 +166,22 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
                             const void* d_q, const void* d_k_store, const void* d_v_store,
                             float scale, hipStream_t stream);
 
+/* Per-layer KV append ([CA]: the per-layer cache write is the single-index
+ * store buffer[layer_id, loc]; the slot bookkeeping lives in the per-step
+ * bind).  Call after paged_decode_bind, which has counted the new token in
+ * seq_lens: the token is position L_b - 1 of request b and its slot is that
+ * request's last kv_indices entry.  Copies
+ *   k_store[layer, slot_b, :, :] = d_k_new[b, :, :]   (and the same for V)
+ * for every request with L_b >= 1 (a request with no tokens is skipped).
+ *   d_k_new, d_v_new   bf16 [batch, n_kv_heads, head_dim], this layer's new rows
+ *   d_k_store, d_v_store  the whole [n_layers, num_slots, n_kv_heads, head_dim]
+ *                      stores, written in place (the library adds the layer
+ *                      offset)
+ * Slots of distinct requests must differ (a valid page table).  One kernel on
+ * `stream`; all pointers 16-byte aligned. */
+pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, const void* d_k_new,
+                                 const void* d_v_new, void* d_k_store, void* d_v_store, hipStream_t stream);
+
 /* Log-sum-exp merge of the S partials into decode_out ([WS]: decode_out is
  * preallocated in the workspace):
  *   out[b,h,:] = sum_j exp(lse_j - LSE) o_j,  LSE = log sum_j exp(lse_j),

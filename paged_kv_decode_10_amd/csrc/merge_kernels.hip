@@ -6,10 +6,11 @@
 // exp(lse_j), out = sum_j exp(lse_j - LSE) o_j; empty splits (lse = -inf)
 // carry no weight and a request with no tokens yields zeros.
 //
-// One wave per (request, query head): lane j reads split j's statistics, the
-// wave reduces max and sum with shuffles, then every lane accumulates its
-// D/64 columns over the non-empty splits (one coalesced row load per split,
-// the loads of a batch issued together).
+// Up to 64 splits: one wave per (request, query head): lane j reads split j's
+// statistics, the wave reduces max and sum with shuffles, then every lane
+// accumulates its D/64 columns over the non-empty splits (one coalesced row
+// load per split, the loads of a batch issued together).  More splits: the
+// workgroup-per-head kernel below.
 #include "pd_internal.h"
 
 namespace pd {
@@ -131,10 +132,89 @@ merge_kernel(MergeArgs a) {
   for (int e = 0; e < E; ++e) out[e] = f32_to_bf16_rne(acc[e] * inv);
 }
 
+// Many splits (S > 64): one workgroup per (request, query head), wave k
+// taking splits [32k, 32k + 32).  Each wave requests its statistics and all
+// of its rows in one round trip, combines them relative to its own maximum,
+// and wave 0 joins the waves' sums through LDS:
+//   M = max_k M_k,  out = sum_k e^(M_k - M) acc_k / sum_k e^(M_k - M) wsum_k.
+constexpr int kWideSplits = 32;  // splits per wave
+constexpr int kWideWaves = 8;    // at most 256 splits
+constexpr int kWideFrom = 64;    // S above which the wide kernel is used: it reads every
+                                 // split's row at once, empty ones too, which costs more
+                                 // than the single wave's second round trip for fewer splits
+
+template <int D>
+__global__ void __launch_bounds__(kWideWaves * 64)
+merge_wide_kernel(MergeArgs a) {
+  constexpr int E = D / 64;
+  __shared__ float s_acc[kWideWaves][D];
+  __shared__ float s_m[kWideWaves], s_w[kWideWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int item = blockIdx.x;
+  const int64_t base = (int64_t)item * a.max_splits;
+  const float* ml = a.ml_part + base * 2;
+  const float* op = a.o_part + base * D;
+  const int j0 = wave * kWideSplits;
+  int n = a.num_splits - j0;  // >= 1: the launch has ceil(S / 32) waves
+  n = n < kWideSplits ? n : kWideSplits;
+  float lse = -INFINITY;
+  if (lane < n) {
+    const float m = ml[2 * (j0 + lane)], ln_l = ml[2 * (j0 + lane) + 1];
+    lse = (m == -INFINITY) ? -INFINITY : m + ln_l;
+  }
+  float v[kWideSplits][E];
+  load_rows<D, kWideSplits>(op, j0, n, lane, v);
+  float M = lse;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float w = (lse == -INFINITY) ? 0.f : __expf(lse - M);
+  float ws = w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 64);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  accumulate<D, kWideSplits>(acc, v, w, 0, n);
+#pragma unroll
+  for (int e = 0; e < E; ++e) s_acc[wave][lane * E + e] = acc[e];
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_w[wave] = ws;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = -INFINITY;
+  for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_m[k]);
+  float tot[E], wsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) tot[e] = 0.f;
+  if (Mt != -INFINITY) {
+    for (int k = 0; k < nw; ++k) {
+      if (s_m[k] == -INFINITY) continue;  // a wave whose splits are all empty
+      const float f = __expf(s_m[k] - Mt);
+      wsum = fmaf(f, s_w[k], wsum);
+#pragma unroll
+      for (int e = 0; e < E; ++e) tot[e] = fmaf(f, s_acc[k][lane * E + e], tot[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  uint16_t* out = a.out + (int64_t)item * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = f32_to_bf16_rne(tot[e] * inv);
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
   const int items = a.batch * a.n_heads;
+  if (a.num_splits > kWideFrom) {
+    const int waves = (a.num_splits + kWideSplits - 1) / kWideSplits;  // <= 8 (S <= 256)
+    if (head_dim == 64)
+      hipLaunchKernelGGL(merge_wide_kernel<64>, dim3(items), dim3(waves * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_wide_kernel<128>, dim3(items), dim3(waves * 64), 0, stream, a);
+    return hipGetLastError();
+  }
   dim3 grid((items + kMergeWaves - 1) / kMergeWaves);
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeWaves * 64), 0, stream, a);

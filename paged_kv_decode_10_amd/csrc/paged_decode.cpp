@@ -213,6 +213,26 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
   return hip_status(pd::launch_attn(a, c.head_dim, stream));
 }
 
+pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, const void* d_k_new,
+                                 const void* d_v_new, void* d_k_store, void* d_v_store, hipStream_t stream) {
+  if (!h || !d_k_new || !d_v_new || !d_k_store || !d_v_store || batch < 1 || layer < 0) return PD_E_INVALID;
+  if (!aligned(d_k_new, 16) || !aligned(d_v_new, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16))
+    return PD_E_INVALID;
+  const pd_config& c = h->cfg;
+  if (batch > c.max_batch || layer >= c.n_layers) return PD_E_CAPACITY;
+  const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
+  pd::AppendArgs a;
+  a.batch = batch;
+  a.row_bytes = c.n_kv_heads * c.head_dim * 2;
+  a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
+  a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
+  a.k_new = static_cast<const uint16_t*>(d_k_new);
+  a.v_new = static_cast<const uint16_t*>(d_v_new);
+  a.k_layer = static_cast<uint16_t*>(d_k_store) + (int64_t)layer * layer_elems;
+  a.v_layer = static_cast<uint16_t*>(d_v_store) + (int64_t)layer * layer_elems;
+  return hip_status(pd::launch_append(a, stream));
+}
+
 pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
                              hipStream_t stream) {
   if (!h || !d_out || batch < 1 || num_splits < 1) return PD_E_INVALID;

@@ -75,7 +75,19 @@ struct MergeArgs {
   uint16_t* out;              // bf16 [batch, n_heads, D]
 };
 
+struct AppendArgs {
+  int32_t batch;
+  int32_t row_bytes;          // n_kv_heads * head_dim * 2
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const uint16_t* k_new;      // bf16 [batch, n_kv_heads, D]
+  const uint16_t* v_new;
+  uint16_t* k_layer;          // bf16 [num_slots, n_kv_heads, D] of this layer
+  uint16_t* v_layer;
+};
+
 hipError_t launch_bind(const BindArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 

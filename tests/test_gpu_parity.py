@@ -30,12 +30,12 @@ def _bind(ws, w, dev, mode=PD_BIND_FULL):
 
 # ------------------------------------------------------------------ tiny ----
 
-@pytest.mark.parametrize("S", [1, 2, 3, 4, 7, 16])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 7, 16, 33, 64, 65])
 def test_tiny_parity(S):
     say(f"[tiny] S={S}")
     w = workloads.make("tiny")
     dev = to_device(w)
-    ws = make_ws(w)
+    ws = make_ws(w, max_splits=128)
     _bind(ws, w, dev)
     torch.cuda.synchronize()
     check_bind(ws, w, w.seq_lens.numpy())
@@ -234,6 +234,18 @@ def test_b1_parity():
     say(f"[b1] auto S={S}")
     check_layer(ws, w, dev, 0, S)
     check_layer(ws, w, dev, 0, 32, parts=False)
+
+
+@pytest.mark.parametrize("S", [0, 65, 97, 255])
+def test_b1_many_splits(S):
+    """Up to 256 splits (the merge spreads a head's splits over several waves)."""
+    w = workloads.make("b1")
+    dev = to_device(w)
+    ws = make_ws(w, max_splits=256)
+    _bind(ws, w, dev)
+    S = ws.num_splits(1, S)
+    say(f"[b1] S={S}")
+    check_layer(ws, w, dev, 0, S)
 
 
 def test_b16_ragged_parity():
