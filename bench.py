@@ -225,6 +225,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--append", choices=("none", "separate", "fused"), default="none",
+                    help="also write each layer's new-token K/V into the cache: its own kernel, or inside the "
+                         "attention launch")
     ap.add_argument("--configs", default="",
                     help="instead of the step: comma-separated workloads (e.g. tiny,b1,b16,long,sweep1,...,sweep32) "
                          "timed one launch at a time with the caches flushed; prints one JSON line")
@@ -275,10 +278,23 @@ def main() -> int:
     S = ws.num_splits(B, args.splits)
     log(f"[bench] splits S={S}")
 
+    if args.append != "none":
+        gen = torch.Generator().manual_seed(123)
+        k_new = torch.randn((NL, B, Hkv, D), generator=gen).to(torch.bfloat16).cuda()
+        v_new = torch.randn((NL, B, Hkv, D), generator=gen).to(torch.bfloat16).cuda()
+
+    def attention(layer):
+        if args.append == "fused":
+            ws.append_attn(B, layer, S, q[layer], k_new[layer], v_new[layer], kst, vst, w.scale)
+        else:
+            if args.append == "separate":
+                ws.append_kv(B, layer, k_new[layer], v_new[layer], kst, vst)
+            ws.attn(B, layer, S, q[layer], kst, vst, w.scale)
+
     def step():
         ws.bind(B, PD_BIND_STEADY, seq, pos, table)
         for layer in range(NL):
-            ws.attn(B, layer, S, q[layer], kst, vst, w.scale)
+            attention(layer)
             ws.merge(B, S, out[layer])
 
     L0 = w.seq_lens.to(torch.int64)
@@ -320,7 +336,10 @@ def main() -> int:
     ag = torch.cuda.CUDAGraph()
     with torch.cuda.graph(ag):
         for layer in range(NL):
-            ws.attn(B, layer, S, q[layer], kst, vst, w.scale)
+            if args.append == "fused":
+                ws.append_attn(B, layer, S, q[layer], k_new[layer], v_new[layer], kst, vst, w.scale)
+            else:
+                ws.attn(B, layer, S, q[layer], kst, vst, w.scale)
     for _ in range(3):
         ag.replay()
     torch.cuda.synchronize()
@@ -333,6 +352,8 @@ def main() -> int:
     attn_us = e0.elapsed_time(e1) * 1e3 / (R * NL)
     Lnow = seq.cpu().to(torch.int64)
     kv_l, alg_l = attn_bytes(Lnow, Hkv, D, B, H, S, w.page_size)
+    if args.append == "fused":
+        alg_l += 2 * 2 * B * Hkv * D * 2  # new K and V rows read and written
     achieved = alg_l / (attn_us * 1e-6) / 1e9
     log(f"[bench] attention kernel: {attn_us:.2f} us/launch, {alg_l / 1e6:.1f} MB algorithmic "
         f"({kv_l / 1e6:.1f} MB KV) -> {achieved:.0f} GB/s")
@@ -343,11 +364,12 @@ def main() -> int:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_digest") == attn_kernel_digest() and tr.get("splits") == S
-                and tr.get("kv_bytes_per_launch") == kv_l):
+                and tr.get("kv_bytes_per_launch") == kv_l and tr.get("kv_append", "none") == args.append):
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "split_attn_kernel<128,4> (paged_decode_attn)", "us_per_launch": round(attn_us, 3),
+                "kernel": ("split_attn_kernel<128,4,true> (paged_decode_append_attn)" if args.append == "fused"
+                           else "split_attn_kernel<128,4,false> (paged_decode_attn)"), "us_per_launch": round(attn_us, 3),
                 "algorithmic_bytes_per_launch": alg_l, "kv_bytes_per_launch": kv_l}
 
     if args.calib_copy_gib > 0:
@@ -370,10 +392,12 @@ def main() -> int:
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode step: 24 layers, B=32, seq_lens~U[1,2048] +1/step, 32 q heads, "
-                               "8 kv heads, head_dim 128, page 16; steady bind + 24 x (split attn, merge), "
-                               "hipGraph replay",
+                               "8 kv heads, head_dim 128, page 16; steady bind + 24 x ("
+                               + {"none": "", "separate": "kv append, ", "fused": "kv append fused into "}[args.append]
+                               + "split attn, merge), hipGraph replay",
                    "batch": B, "n_layers": NL, "n_heads": H, "n_kv_heads": Hkv, "head_dim": D,
-                   "page_size": w.page_size, "num_splits": S, "parallelism": "single GPU",
+                   "page_size": w.page_size, "num_splits": S, "kv_append": args.append,
+                   "parallelism": "single GPU",
                    "accumulate": "fp32"},
         "us_per_layer": round(ms_step * 1e3 / NL, 3),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -182,6 +182,15 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
 pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, const void* d_k_new,
                                  const void* d_v_new, void* d_k_store, void* d_v_store, hipStream_t stream);
 
+/* The KV append fused into the attention launch: the same writes as
+ * paged_decode_append_kv followed by the same partials as paged_decode_attn
+ * (bit for bit), in one kernel.  The wave that reads a row's newest token takes
+ * its K/V from d_k_new / d_v_new and writes them into the stores, so no wave
+ * reads a slot while it is being written.  Arguments as in those two calls. */
+pd_status paged_decode_append_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
+                                   const void* d_q, const void* d_k_new, const void* d_v_new,
+                                   void* d_k_store, void* d_v_store, float scale, hipStream_t stream);
+
 /* Log-sum-exp merge of the S partials into decode_out ([WS]: decode_out is
  * preallocated in the workspace):
  *   out[b,h,:] = sum_j exp(lse_j - LSE) o_j,  LSE = log sum_j exp(lse_j),

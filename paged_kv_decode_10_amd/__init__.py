@@ -182,6 +182,22 @@ class PagedDecode:
                    _abi.lib().paged_decode_append_kv(self._h, batch, layer, p_kn, p_vn, p_k, p_v,
                                                      _stream_ptr(stream)))
 
+    def append_attn(self, batch: int, layer: int, num_splits: int, q: torch.Tensor, k_new: torch.Tensor,
+                    v_new: torch.Tensor, k_store: torch.Tensor, v_store: torch.Tensor, scale: float,
+                    stream=None) -> None:
+        """append_kv() and attn() in one launch (bit-identical results)."""
+        c = self.cfg
+        store_numel = c.n_layers * c.num_slots * c.n_kv_heads * c.head_dim
+        row = batch * c.n_kv_heads * c.head_dim
+        p_q = _dev_ptr(q, torch.bfloat16, "q", batch * c.n_heads * c.head_dim)
+        p_kn = _dev_ptr(k_new, torch.bfloat16, "k_new", row)
+        p_vn = _dev_ptr(v_new, torch.bfloat16, "v_new", row)
+        p_k = _dev_ptr(k_store, torch.bfloat16, "k_store", store_numel)
+        p_v = _dev_ptr(v_store, torch.bfloat16, "v_store", store_numel)
+        _abi.check("paged_decode_append_attn",
+                   _abi.lib().paged_decode_append_attn(self._h, batch, layer, num_splits, p_q, p_kn, p_vn, p_k,
+                                                       p_v, float(scale), _stream_ptr(stream)))
+
     def merge(self, batch: int, num_splits: int, out: torch.Tensor, stream=None) -> None:
         c = self.cfg
         p_o = _dev_ptr(out, torch.bfloat16, "out", batch * c.n_heads * c.head_dim)

@@ -28,6 +28,7 @@ EXPORTS = (
     "paged_decode_bind",
     "paged_decode_attn",
     "paged_decode_append_kv",
+    "paged_decode_append_attn",
     "paged_decode_merge",
     "paged_decode_read_error",
     "paged_decode_destroy",
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "paged_decode_bind": [P, I32, I32, P, P, P, P],
         "paged_decode_attn": [P, I32, I32, I32, P, P, P, F, P],
         "paged_decode_append_kv": [P, I32, I32, P, P, P, P, P],
+        "paged_decode_append_attn": [P, I32, I32, I32, P, P, P, P, P, F, P],
         "paged_decode_merge": [P, I32, I32, P, P],
         "paged_decode_read_error": [P, ctypes.POINTER(ctypes.c_uint32), P],
         "paged_decode_destroy": [P],

@@ -93,6 +93,7 @@ struct Unit {
   int last;    // last unit of a row segment: write the split
   int row_end; // the segment ends the row: splits after it are empty
   int ntok;    // valid tokens in the unit (lanes c < ntok)
+  int newtok;  // index in the unit of the row's newest token (position L - 1), else -1
   int b, g, j;   // g: the wave's kv head
   int32_t slot;  // per lane: slot of token c (a real row of the request)
 };
@@ -166,6 +167,8 @@ struct Producer {
     const int tok_lo = lp * ps + piece * ut;
     const int tok_hi = min(lp * ps + min((piece + 1) * ut, ps), L);
     u.ntok = done ? 0 : tok_hi - tok_lo;
+    // (a trailing 16-token piece of a page past the row's end holds no token)
+    u.newtok = (!done && tok_lo <= L - 1 && tok_hi == L) ? L - 1 - tok_lo : -1;
     // Lanes past the unit's tokens (and every lane past the end of the work)
     // read a real token of the row instead; their scores are masked.
     const int t_last = (!done && u.ntok > 0) ? tok_hi - 1 : L - 1;
@@ -201,12 +204,18 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) { return *p; }
 __device__ __forceinline__ uint2 ld_stream(const uint2* p) { return *p; }
 #endif
 
-template <int D>
+// With APPEND the row's newest token is read from the new-row buffer (the
+// store still holds its old contents until this launch writes them).
+template <int D, bool APPEND>
 __device__ __forceinline__ Tile<D> load_tile(const AttnArgs& a, const Unit& u, int GP, int r, int c) {
   Tile<D> t;
   constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
   const int64_t stride = (int64_t)a.n_kv_heads * D;
   const uint16_t* kp = a.k_layer + (int64_t)u.slot * stride + (int64_t)u.g * D + 8 * r;
+  if constexpr (APPEND) {
+    const uint16_t* kn = a.k_new + ((int64_t)u.b * a.n_kv_heads + u.g) * D + 8 * r;
+    kp = (c == u.newtok) ? kn : kp;
+  }
   // K and V are read exactly once: streaming (non-temporal) loads keep them
   // from evicting the q rows and the index lists from the caches.
 #pragma unroll
@@ -215,6 +224,10 @@ __device__ __forceinline__ Tile<D> load_tile(const AttnArgs& a, const Unit& u, i
   for (int i = 0; i < 4; ++i) {
     const int32_t sv = __shfl(u.slot, 4 * r + i, 64);
     const uint16_t* vp = a.v_layer + (int64_t)sv * stride + (int64_t)u.g * D + VE * c;
+    if constexpr (APPEND) {
+      const uint16_t* vn = a.v_new + ((int64_t)u.b * a.n_kv_heads + u.g) * D + VE * c;
+      vp = (4 * r + i == u.newtok) ? vn : vp;
+    }
     if constexpr (VE == 8) t.v[i].u = ld_stream(reinterpret_cast<const uint4*>(vp));
     else t.v[i].u = ld_stream(reinterpret_cast<const uint2*>(vp));
   }
@@ -245,7 +258,7 @@ __device__ unsigned long long g_pd_trace[kSplitChunks * 8];
   } while (0)
 #endif
 
-template <int D, int GP>
+template <int D, int GP, bool APPEND>
 __global__ void __launch_bounds__(kThreads, 2)
 split_attn_kernel(AttnArgs a) {
   constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
@@ -411,6 +424,33 @@ split_attn_kernel(AttnArgs a) {
 
   auto compute = [&](const Tile<D>& T, const Unit& u) {
     if (u.first) reset();
+    if (APPEND && u.newtok >= 0) {
+      // Fused KV append: this unit holds the row's newest token, which the
+      // tile took from the new-row buffer (nobody reads its slot in the store
+      // during this launch).  The lanes that hold its K and V chunks store
+      // them at that slot, straight from the tile's registers.
+      const int64_t row = (__shfl(u.slot, u.newtok, 64) * (int64_t)a.n_kv_heads + u.g) * D;
+      if (c == u.newtok) {  // lanes 16r + newtok: 16-byte K chunks at 16r + 64s
+        uint16_t* kd = a.k_dst + row + 8 * r;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4*>(kd + 32 * s) = T.k[s];
+      }
+      if (r == (u.newtok >> 2)) {  // row group of token 4r + i: V chunk VE*c
+        const int i = u.newtok & 3;
+        auto pick = [&](uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+          return i == 0 ? x0 : i == 1 ? x1 : i == 2 ? x2 : x3;
+        };
+        uint16_t* vd = a.v_dst + row + VE * c;
+        if constexpr (VE == 8) {
+          *reinterpret_cast<uint4*>(vd) = make_uint4(
+              pick(T.v[0].u.x, T.v[1].u.x, T.v[2].u.x, T.v[3].u.x), pick(T.v[0].u.y, T.v[1].u.y, T.v[2].u.y, T.v[3].u.y),
+              pick(T.v[0].u.z, T.v[1].u.z, T.v[2].u.z, T.v[3].u.z), pick(T.v[0].u.w, T.v[1].u.w, T.v[2].u.w, T.v[3].u.w));
+        } else {
+          *reinterpret_cast<uint2*>(vd) = make_uint2(pick(T.v[0].u.x, T.v[1].u.x, T.v[2].u.x, T.v[3].u.x),
+                                                     pick(T.v[0].u.y, T.v[1].u.y, T.v[2].u.y, T.v[3].u.y));
+        }
+      }
+    }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -464,19 +504,19 @@ split_attn_kernel(AttnArgs a) {
   Unit uB = pr.next(c);
   Unit uC = pr.next(c);
   Unit uD = pr.next(c);
-  Tile<D> TA = load_tile<D>(a, uA, GP, r, c);
-  Tile<D> TB = load_tile<D>(a, uB, GP, r, c);
+  Tile<D> TA = load_tile<D, APPEND>(a, uA, GP, r, c);
+  Tile<D> TB = load_tile<D, APPEND>(a, uB, GP, r, c);
   int nunits = 0;
   while (uA.valid) {
     compute(TA, uA);
     if (nunits++ == 0) PD_STAMP(2, wall_clock64());
-    TA = load_tile<D>(a, uC, GP, r, c);
+    TA = load_tile<D, APPEND>(a, uC, GP, r, c);
     uA = uC;
     uC = pr.next(c);
     if (!uB.valid) break;
     compute(TB, uB);
     ++nunits;
-    TB = load_tile<D>(a, uD, GP, r, c);
+    TB = load_tile<D, APPEND>(a, uD, GP, r, c);
     uB = uD;
     uD = pr.next(c);
   }
@@ -496,7 +536,10 @@ split_attn_kernel(AttnArgs a) {
 
 template <int D, int GP>
 hipError_t launch_dg(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((split_attn_kernel<D, GP>), dim3(kSplitChunks / kWaves), dim3(kThreads), 0, stream, a);
+  if (a.k_new != nullptr)
+    hipLaunchKernelGGL((split_attn_kernel<D, GP, true>), dim3(kSplitChunks / kWaves), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((split_attn_kernel<D, GP, false>), dim3(kSplitChunks / kWaves), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

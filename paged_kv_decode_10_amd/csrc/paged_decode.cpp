@@ -180,13 +180,20 @@ pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* 
   return hip_status(pd::launch_bind(a, stream));
 }
 
-pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
-                            const void* d_q, const void* d_k_store, const void* d_v_store,
-                            float scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by paged_decode_attn and paged_decode_append_attn (k_new == nullptr:
+// no append).
+pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
+                      const void* d_k_new, const void* d_v_new, const void* d_k_store,
+                      const void* d_v_store, float scale, hipStream_t stream) {
   if (!h || !d_q || !d_k_store || !d_v_store || batch < 1 || num_splits < 1 || layer < 0)
     return PD_E_INVALID;
   if (!aligned(d_q, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16))
     return PD_E_INVALID;
+  if (d_k_new && (!aligned(d_k_new, 16) || !aligned(d_v_new, 16))) return PD_E_INVALID;
   const pd_config& c = h->cfg;
   if (batch > c.max_batch || num_splits > c.max_splits || layer >= c.n_layers)
     return PD_E_CAPACITY;
@@ -210,7 +217,28 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
   a.meta = at<int32_t>(h, h->lay.meta);
   a.o_part = at<float>(h, h->lay.o_part);
   a.ml_part = at<float>(h, h->lay.ml_part);
+  a.k_new = static_cast<const uint16_t*>(d_k_new);
+  a.v_new = static_cast<const uint16_t*>(d_v_new);
+  a.k_dst = const_cast<uint16_t*>(a.k_layer);
+  a.v_dst = const_cast<uint16_t*>(a.v_layer);
   return hip_status(pd::launch_attn(a, c.head_dim, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
+                            const void* d_q, const void* d_k_store, const void* d_v_store,
+                            float scale, hipStream_t stream) {
+  return attn_launch(h, batch, layer, num_splits, d_q, nullptr, nullptr, d_k_store, d_v_store, scale, stream);
+}
+
+pd_status paged_decode_append_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
+                                   const void* d_q, const void* d_k_new, const void* d_v_new,
+                                   void* d_k_store, void* d_v_store, float scale, hipStream_t stream) {
+  if (!d_k_new || !d_v_new) return PD_E_INVALID;
+  return attn_launch(h, batch, layer, num_splits, d_q, d_k_new, d_v_new, d_k_store, d_v_store, scale, stream);
 }
 
 pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, const void* d_k_new,

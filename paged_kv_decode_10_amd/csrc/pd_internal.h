@@ -63,6 +63,13 @@ struct AttnArgs {
   const int32_t* meta;
   float* o_part;              // [max_batch, n_heads, max_splits, D]
   float* ml_part;             // [max_batch, n_heads, max_splits, 2]
+  // KV append fused into the launch (null when not appending): the new
+  // token's rows, bf16 [batch, n_kv_heads, D], and the writable layer stores
+  // (the same addresses as k_layer / v_layer).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_dst;
+  uint16_t* v_dst;
 };
 
 struct MergeArgs {

@@ -147,3 +147,92 @@ def test_graph_step_with_append_matches_eager():
     for i, (a, b) in enumerate(zip(eager, graph)):
         assert torch.equal(_bits(a), _bits(b)), f"step {i}"
     assert torch.equal(_bits(ke), _bits(kg)) and torch.equal(_bits(ve), _bits(vg))
+
+
+@pytest.mark.parametrize("hkv,D,ps,S", [(4, 128, 16, 0), (2, 64, 7, 5), (8, 128, 1, 17), (4, 128, 32, 3),
+                                        (1, 64, 32, 1), (8, 128, 16, 64)])
+def test_fused_append_attn_bit_identical(hkv, D, ps, S):
+    """append_attn == append_kv + attn: stores, partial statistics and decode_out, bit for bit."""
+    say(f"[append fused] hkv={hkv} D={D} ps={ps} S={S}")
+    w = workloads.make_custom("appf", seed=50 + hkv + ps + S, n_layers=2,
+                              seq_lens=[5, 0, 130, 17, 1, 64, 47, 33, 16, 32],
+                              n_heads=4 * hkv, n_kv_heads=hkv, head_dim=D, page_size=ps, growth=2)
+    B = w.batch
+    kn, vn = _new_rows(w, 5)
+    results = []
+    for fused in (False, True):
+        dev = to_device(w)
+        ws = make_ws(w)
+        S_ = ws.num_splits(B, S)
+        out = torch.empty((B, w.n_heads, D), dtype=torch.bfloat16, device="cuda")
+        ws.bind(B, PD_BIND_FULL, dev.seq_lens, dev.position_ids, dev.req_to_page)
+        ws.bind(B, PD_BIND_STEADY, dev.seq_lens, dev.position_ids, dev.req_to_page)
+        layer = 1
+        if fused:
+            ws.append_attn(B, layer, S_, dev.q[layer], kn[layer].cuda(), vn[layer].cuda(), dev.k, dev.v, w.scale)
+        else:
+            ws.append_kv(B, layer, kn[layer].cuda(), vn[layer].cuda(), dev.k, dev.v)
+            ws.attn(B, layer, S_, dev.q[layer], dev.k, dev.v, w.scale)
+        ws.merge(B, S_, out)
+        torch.cuda.synchronize()
+        results.append((out.cpu(), ws.ml_part[:B, :, :S_].cpu(), dev.k.cpu(), dev.v.cpu()))
+    (o0, m0, k0, v0), (o1, m1, k1, v1) = results
+    assert torch.equal(_bits(k0), _bits(k1)) and torch.equal(_bits(v0), _bits(v1)), "stores differ"
+    assert torch.equal(m0.view(torch.int32), m1.view(torch.int32)), "partial statistics differ"
+    assert torch.equal(_bits(o0), _bits(o1)), "decode_out differs"
+    L = w.seq_lens.numpy() + 1
+    _, _, ref = _oracle_step(w, w.k_store, w.v_store, L, kn, vn, 1)
+    assert_close_out(o1.float().numpy(), ref, "fused decode_out")
+
+
+def test_fused_graph_step_matches_eager():
+    say("[append fused] graph")
+    w = workloads.make_custom("appfg", seed=46, n_layers=3,
+                              seq_lens=lambda g: torch.randint(0, 500, (9,), generator=g).tolist(),
+                              n_heads=32, n_kv_heads=8, head_dim=128, page_size=16, growth=8)
+    B = w.batch
+    kn, vn = _new_rows(w, 6)
+
+    def run(fused, graph):
+        dev = to_device(w)
+        ws = make_ws(w)
+        S = ws.num_splits(B)
+        kn_d, vn_d = kn.cuda(), vn.cuda()
+        out = torch.empty((w.n_layers, B, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        ws.bind(B, PD_BIND_FULL, dev.seq_lens, dev.position_ids, dev.req_to_page)
+
+        def step():
+            ws.bind(B, PD_BIND_STEADY, dev.seq_lens, dev.position_ids, dev.req_to_page)
+            for layer in range(w.n_layers):
+                if fused:
+                    ws.append_attn(B, layer, S, dev.q[layer], kn_d[layer], vn_d[layer], dev.k, dev.v, w.scale)
+                else:
+                    ws.append_kv(B, layer, kn_d[layer], vn_d[layer], dev.k, dev.v)
+                    ws.attn(B, layer, S, dev.q[layer], dev.k, dev.v, w.scale)
+                ws.merge(B, S, out[layer])
+
+        outs = []
+        step()
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+        for i in range(3):
+            kn_d.add_(1.0 / 64)
+            vn_d.sub_(1.0 / 64)
+            if graph:
+                g.replay()
+            else:
+                step()
+            torch.cuda.synchronize()
+            outs.append(out.clone())
+        return outs, dev.k.cpu(), dev.v.cpu()
+
+    ref, kr, vr = run(False, False)
+    for fused, graph in ((True, False), (True, True)):
+        got, kg, vg = run(fused, graph)
+        for i, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(_bits(a), _bits(b)), f"fused={fused} graph={graph} step {i}"
+        assert torch.equal(_bits(kr), _bits(kg)) and torch.equal(_bits(vr), _bits(vg))
