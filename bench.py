@@ -147,7 +147,8 @@ def config_sweep(names, reps: int, oracle_budget: float):
     rows = []
     for name in names:
         t0 = time.perf_counter()
-        w = workloads.make(name)
+        base_name, _, layout = name.partition("@")  # "b16@contiguous": the contiguous-cache layout
+        w = workloads.make(base_name, layout=layout or "paged")
         B, H, Hkv, D = w.batch, w.n_heads, w.n_kv_heads, w.head_dim
         cfg = Config(n_layers=w.n_layers, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size,
                      max_batch=B, max_splits=256, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
@@ -157,7 +158,10 @@ def config_sweep(names, reps: int, oracle_budget: float):
         q, kst, vst = w.q.cuda(), w.k_store.cuda(), w.v_store.cuda()
         out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
         S = ws.num_splits(B)
-        ws.bind(B, PD_BIND_FULL, seq, pos, tab)
+        if layout == "contiguous":
+            ws.bind_contiguous(B, PD_BIND_FULL, seq, pos, w.meta["req_base"].cuda())
+        else:
+            ws.bind(B, PD_BIND_FULL, seq, pos, tab)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ta, tm = [], []
         for r in range(reps + 2):
@@ -229,8 +233,9 @@ def main() -> int:
                     help="also write each layer's new-token K/V into the cache: its own kernel, or inside the "
                          "attention launch")
     ap.add_argument("--configs", default="",
-                    help="instead of the step: comma-separated workloads (e.g. tiny,b1,b16,long,sweep1,...,sweep32) "
-                         "timed one launch at a time with the caches flushed; prints one JSON line")
+                    help="instead of the step: comma-separated workloads (e.g. tiny,b1,b16,long,sweep1,...,sweep32; "
+                         "NAME@contiguous for the contiguous-cache layout) timed one launch at a time with the "
+                         "caches flushed; prints one JSON line")
     ap.add_argument("--config-reps", type=int, default=20)
     ap.add_argument("--oracle-budget", type=float, default=0.0,
                     help="with --configs: seconds of oracle timing per config (0 = none)")

@@ -142,6 +142,18 @@ pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* 
                             int32_t* d_position_ids, const int32_t* d_req_to_page,
                             hipStream_t stream);
 
+/* The same bind for a contiguous cache ([CA]: a contiguous per-request buffer
+ * next to the paged one): request b's tokens occupy slots base_b, base_b + 1,
+ * ... of the stores, so kv_indices[kv_indptr[b] + t] = d_req_base[b] + t.
+ *   d_req_base  int32 [batch]: the first slot of each request's buffer
+ * Lengths are capped at max_pages_per_req * page_size as in the paged bind
+ * (the per-request capacity); a token whose slot falls outside
+ * [0, num_slots) sets PD_ERR_BAD_PAGE and reads slot 0.  The split plan and
+ * the attention are unchanged (they count pages of page_size tokens). */
+pd_status paged_decode_bind_contiguous(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
+                                       int32_t* d_position_ids, const int32_t* d_req_base,
+                                       hipStream_t stream);
+
 /* Split-KV attention for one layer ([WS]: attn_paged_decode writes split
  * partials into decode_o_part / decode_ml_part).
  *   d_q        bf16 [batch, n_heads, head_dim] queries of this layer

@@ -28,6 +28,7 @@ from .paged_attention import (  # noqa: F401
     gather_rows,
     kv_team,
     kv_indices,
+    kv_indices_contiguous,
     kv_indptr,
     merge_splits,
     SPLIT_CHUNKS,

@@ -87,6 +87,15 @@ def kv_indices(seq_lens, req_to_page, page_size: int) -> np.ndarray:
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
 
 
+def kv_indices_contiguous(seq_lens, req_base) -> np.ndarray:
+    """Contiguous cache ([CA] bullet adding a contiguous per-request buffer next
+    to the paged cache): request b's t-th token is at slot req_base[b] + t."""
+    L = np.asarray(seq_lens).reshape(-1).astype(np.int64)
+    base = np.asarray(req_base).reshape(-1).astype(np.int64)
+    parts = [base[b] + np.arange(L[b], dtype=np.int64) for b in range(len(L))]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
 def bind_steady(seq_lens, position_ids):
     """Steady decode step: every request gained exactly one token."""
     return (np.asarray(seq_lens).astype(np.int64) + 1,

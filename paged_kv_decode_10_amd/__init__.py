@@ -157,6 +157,16 @@ class PagedDecode:
         _abi.check("paged_decode_bind",
                    _abi.lib().paged_decode_bind(self._h, batch, mode, p_sl, p_pos, p_tab, _stream_ptr(stream)))
 
+    def bind_contiguous(self, batch: int, mode: int, seq_lens: torch.Tensor, position_ids,
+                        req_base: torch.Tensor, stream=None) -> None:
+        """Bind for a contiguous cache: request b's tokens sit at slots req_base[b] + t."""
+        p_sl = _dev_ptr(seq_lens, torch.int32, "seq_lens", batch)
+        p_pos = None if position_ids is None else _dev_ptr(position_ids, torch.int32, "position_ids", batch)
+        p_base = _dev_ptr(req_base, torch.int32, "req_base", batch)
+        _abi.check("paged_decode_bind_contiguous",
+                   _abi.lib().paged_decode_bind_contiguous(self._h, batch, mode, p_sl, p_pos, p_base,
+                                                           _stream_ptr(stream)))
+
     def attn(self, batch: int, layer: int, num_splits: int, q: torch.Tensor, k_store: torch.Tensor,
              v_store: torch.Tensor, scale: float, stream=None) -> None:
         c = self.cfg

@@ -26,6 +26,7 @@ EXPORTS = (
     "paged_decode_layout",
     "paged_decode_num_splits",
     "paged_decode_bind",
+    "paged_decode_bind_contiguous",
     "paged_decode_attn",
     "paged_decode_append_kv",
     "paged_decode_append_attn",
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "paged_decode_layout": [P, ctypes.POINTER(PdLayout)],
         "paged_decode_num_splits": [P, I32, I32, ctypes.POINTER(I32)],
         "paged_decode_bind": [P, I32, I32, P, P, P, P],
+        "paged_decode_bind_contiguous": [P, I32, I32, P, P, P, P],
         "paged_decode_attn": [P, I32, I32, I32, P, P, P, F, P],
         "paged_decode_append_kv": [P, I32, I32, P, P, P, P, P],
         "paged_decode_append_attn": [P, I32, I32, I32, P, P, P, P, P, F, P],

@@ -99,24 +99,40 @@ constexpr int kFillThreads = 256;
 
 // Grid (batch, Y): block (b, y) fills tokens y*256 + tid, stepping 256*Y, of
 // request b.  The token range comes from the (already clipped) kv_indptr.
+// Paged cache: slot = page * page_size + t % page_size through the request's
+// page list.  Contiguous cache (AstrAI cache.py view: a contiguous per-request
+// buffer next to the paged one): slot = base_b + t.
 __global__ void __launch_bounds__(kFillThreads)
 bind_fill_kernel(BindArgs a) {
   const int b = blockIdx.x;
   const int32_t start = a.kv_indptr[b];
   const int32_t len = a.kv_indptr[b + 1] - start;
-  const int32_t* row = a.req_to_page + (int64_t)b * a.max_pages_per_req;
   uint32_t flags = 0;
-  for (int32_t t = blockIdx.y * kFillThreads + threadIdx.x; t < len;
-       t += kFillThreads * gridDim.y) {
-    const int32_t page = row[t / a.page_size];
-    int64_t slot;
-    if (page < 0 || (int64_t)page >= a.num_pages) {
-      flags |= PD_ERR_BAD_PAGE;
-      slot = 0;
-    } else {
-      slot = (int64_t)page * a.page_size + t % a.page_size;
+  if (a.req_base != nullptr) {
+    const int64_t base = a.req_base[b];
+    for (int32_t t = blockIdx.y * kFillThreads + threadIdx.x; t < len;
+         t += kFillThreads * gridDim.y) {
+      int64_t slot = base + t;
+      if (base < 0 || slot >= a.num_slots) {
+        flags |= PD_ERR_BAD_PAGE;
+        slot = 0;
+      }
+      a.kv_indices[start + t] = (int32_t)slot;
     }
-    a.kv_indices[start + t] = (int32_t)slot;
+  } else {
+    const int32_t* row = a.req_to_page + (int64_t)b * a.max_pages_per_req;
+    for (int32_t t = blockIdx.y * kFillThreads + threadIdx.x; t < len;
+         t += kFillThreads * gridDim.y) {
+      const int32_t page = row[t / a.page_size];
+      int64_t slot;
+      if (page < 0 || (int64_t)page >= a.num_pages) {
+        flags |= PD_ERR_BAD_PAGE;
+        slot = 0;
+      } else {
+        slot = (int64_t)page * a.page_size + t % a.page_size;
+      }
+      a.kv_indices[start + t] = (int32_t)slot;
+    }
   }
   if (flags) atomicOr(a.error_word, flags);
 }

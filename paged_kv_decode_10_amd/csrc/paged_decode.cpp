@@ -152,14 +152,17 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t req
   return PD_OK;
 }
 
-pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
-                            int32_t* d_position_ids, const int32_t* d_req_to_page,
-                            hipStream_t stream) {
-  if (!h || !d_seq_lens || !d_req_to_page || batch < 1) return PD_E_INVALID;
+}  // extern "C"
+
+namespace {
+
+pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens, int32_t* d_position_ids,
+                      const int32_t* d_req_to_page, const int32_t* d_req_base, hipStream_t stream) {
+  if (!h || !d_seq_lens || (!d_req_to_page && !d_req_base) || batch < 1) return PD_E_INVALID;
   if (mode != PD_BIND_FULL && mode != PD_BIND_STEADY) return PD_E_INVALID;
   if (mode == PD_BIND_STEADY && !d_position_ids) return PD_E_INVALID;
-  if (!aligned(d_seq_lens, 4) || !aligned(d_req_to_page, 4) ||
-      (d_position_ids && !aligned(d_position_ids, 4)))
+  if (!aligned(d_seq_lens, 4) || (d_req_to_page && !aligned(d_req_to_page, 4)) ||
+      (d_req_base && !aligned(d_req_base, 4)) || (d_position_ids && !aligned(d_position_ids, 4)))
     return PD_E_INVALID;
   if (batch > h->cfg.max_batch) return PD_E_CAPACITY;
   pd::BindArgs a;
@@ -168,16 +171,36 @@ pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* 
   a.page_size = h->cfg.page_size;
   a.max_pages_per_req = h->cfg.max_pages_per_req;
   a.num_pages = h->cfg.num_slots / h->cfg.page_size;
+  a.num_slots = h->cfg.num_slots;
   a.max_total_tokens = h->cfg.max_total_tokens;
   a.seq_lens = d_seq_lens;
   a.position_ids = d_position_ids;
   a.req_to_page = d_req_to_page;
+  a.req_base = d_req_base;
   a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
   a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
   a.page_indptr = at<int32_t>(h, h->lay.page_indptr);
   a.meta = at<int32_t>(h, h->lay.meta);
   a.error_word = at<uint32_t>(h, h->lay.error_word);
   return hip_status(pd::launch_bind(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
+                            int32_t* d_position_ids, const int32_t* d_req_to_page,
+                            hipStream_t stream) {
+  if (!d_req_to_page) return PD_E_INVALID;
+  return bind_launch(h, batch, mode, d_seq_lens, d_position_ids, d_req_to_page, nullptr, stream);
+}
+
+pd_status paged_decode_bind_contiguous(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
+                                       int32_t* d_position_ids, const int32_t* d_req_base,
+                                       hipStream_t stream) {
+  if (!d_req_base) return PD_E_INVALID;
+  return bind_launch(h, batch, mode, d_seq_lens, d_position_ids, nullptr, d_req_base, stream);
 }
 
 }  // extern "C"

@@ -36,7 +36,9 @@ struct BindArgs {
   int64_t max_total_tokens;
   int32_t* seq_lens;
   int32_t* position_ids;      // may be null
-  const int32_t* req_to_page;
+  const int32_t* req_to_page;  // paged cache: [batch, max_pages_per_req] page ids
+  const int32_t* req_base;     // contiguous cache: [batch] first slot of each request (else null)
+  int64_t num_slots;
   int32_t* kv_indptr;
   int32_t* kv_indices;
   int32_t* page_indptr;       // [batch + 1]: prefix sum of ceil(L_b / page_size)

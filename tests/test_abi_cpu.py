@@ -79,6 +79,7 @@ def test_host_side_rejections(abi):
     s = ctypes.c_int32()
     assert L.paged_decode_num_splits(None, 1, 0, ctypes.byref(s)) == abi.PD_E_INVALID
     assert L.paged_decode_bind(None, 1, 0, None, None, None, None) == abi.PD_E_INVALID
+    assert L.paged_decode_bind_contiguous(None, 1, 0, None, None, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_attn(None, 1, 0, 1, None, None, None, 1.0, None) == abi.PD_E_INVALID
     assert L.paged_decode_merge(None, 1, 1, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_kv(None, 1, 0, None, None, None, None, None) == abi.PD_E_INVALID

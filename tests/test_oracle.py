@@ -72,6 +72,25 @@ def test_bind_golden():
         g["steady"]["append_slots"]
 
 
+def test_contiguous_bind_golden():
+    g = _load("contiguous_example.json")
+    assert oracle.kv_indptr(g["seq_lens"]).tolist() == g["kv_indptr"]
+    assert oracle.kv_indices_contiguous(g["seq_lens"], g["req_base"]).tolist() == g["kv_indices"]
+
+
+@pytest.mark.parametrize("ps", [1, 4, 16])
+def test_contiguous_equals_paged_with_consecutive_pages(ps):
+    """A contiguous buffer that starts on a page boundary is the paged cache
+    whose page list is consecutive pages."""
+    rng = np.random.default_rng(ps)
+    lens = [int(x) for x in rng.integers(0, 60, size=5)]
+    width = max(-(-x // ps) for x in lens) + 1
+    first_page = rng.permutation(5) * width
+    base = first_page * ps
+    table = first_page[:, None] + np.arange(width)[None, :]
+    assert oracle.kv_indices_contiguous(lens, base).tolist() == oracle.kv_indices(lens, table, ps).tolist()
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_append_slots_brute_force(seed):
     """The newest token's slot, found another way: walk the request's pages in

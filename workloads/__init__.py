@@ -83,7 +83,7 @@ def _fill_store(gen, n_layers, num_slots, hkv, d, chunk_rows=1 << 16):
 def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim,
                 page_size=16, num_pages=None, pool_factor=1.25, growth=0,
                 max_pages_per_req=None, q_scale=1.0, scale=None,
-                nan_unassigned=True, shuffle=True):
+                nan_unassigned=True, shuffle=True, layout="paged"):
     """Build a workload.
 
     ``seq_lens`` is either a list of ints or a callable ``gen -> list`` that
@@ -92,19 +92,35 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
     steps that add one token each), so steady-state steps need no new pages.
     ``shuffle=False`` assigns pages in order instead of by the seeded
     permutation (a locality experiment; the named workloads shuffle).
+    ``layout="contiguous"`` gives every request one contiguous region of
+    max_pages_per_req pages instead (regions in a seeded random order, plus
+    one spare region of NaN); ``meta["req_base"]`` holds each request's first
+    slot, and ``req_to_page`` lists the region's pages in order.
     """
     gen = torch.Generator().manual_seed(seed)
     lens = list(seq_lens(gen)) if callable(seq_lens) else list(seq_lens)
     B = len(lens)
     pages_b = _pages_needed([x + growth for x in lens], page_size)
+    if layout == "contiguous":
+        mppr = max_pages_per_req if max_pages_per_req is not None else max(1, max(pages_b))
+        if mppr < max(pages_b):
+            raise ValueError("max_pages_per_req smaller than a request's page count")
+        pages_b = [mppr] * B
+        num_pages = (B + 1) * mppr
+        regions = torch.randperm(B + 1, generator=gen).to(torch.int32)
+        perm = (regions[:, None] * mppr + torch.arange(mppr, dtype=torch.int32)[None, :]).flatten()
+        max_pages_per_req = mppr
+    elif layout != "paged":
+        raise ValueError(f"unknown layout {layout}")
     total_pages = sum(pages_b)
     if num_pages is None:
         num_pages = max(total_pages, math.ceil(pool_factor * (sum(lens) + growth * B) / page_size))
     if num_pages < total_pages:
         raise ValueError("pool too small for the requested lengths")
-    perm = torch.randperm(num_pages, generator=gen).to(torch.int32)
-    if not shuffle:  # contiguous page assignment (same draw order, permutation unused)
-        perm = torch.arange(num_pages, dtype=torch.int32)
+    if layout == "paged":
+        perm = torch.randperm(num_pages, generator=gen).to(torch.int32)
+        if not shuffle:  # pages in order (same draw order, permutation unused)
+            perm = torch.arange(num_pages, dtype=torch.int32)
     mppr = max_pages_per_req if max_pages_per_req is not None else max(1, max(pages_b))
     if mppr < max(pages_b):
         raise ValueError("max_pages_per_req smaller than a request's page count")
@@ -136,7 +152,9 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
                     num_pages=num_pages, max_pages_per_req=mppr, scale=float(torch.tensor(scale, dtype=torch.float32)),
                     seq_lens=seq, position_ids=(seq - 1).clamp(min=0), req_to_page=req_to_page,
                     q=q, k_store=k_store, v_store=v_store,
-                    meta={"seed": seed, "growth": growth, "q_scale": q_scale})
+                    meta={"seed": seed, "growth": growth, "q_scale": q_scale, "layout": layout,
+                          "req_base": (req_to_page[:, 0].to(torch.int32) * page_size if layout == "contiguous"
+                                       else None)})
 
 
 def _uniform_lens(B, lo, hi):
