@@ -211,6 +211,62 @@ pd_status paged_decode_append_attn(pd_handle* h, int32_t batch, int32_t layer, i
 pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
                              hipStream_t stream);
 
+/* ---- Batch-size graph pool ([EX]: graphs pre-captured at init for
+ * power-of-two batch sizes, one graph per batch-size key with all inputs at
+ * fixed workspace addresses, a warmup -> capture -> replay lifecycle, graphs
+ * used only when warmup succeeds) ---- */
+
+/* The caller's fixed buffers of a decode step, each sized for max_batch. */
+typedef struct pd_step_buffers {
+  int32_t* seq_lens;          /* int32 [max_batch], advanced +1 per step       */
+  int32_t* position_ids;      /* int32 [max_batch], advanced +1 per step       */
+  const int32_t* req_to_page; /* int32 [max_batch, max_pages_per_req] (paged)  */
+  const int32_t* req_base;    /* int32 [max_batch] (contiguous); exactly one of
+                                 req_to_page and req_base is non-NULL           */
+  const void* q;              /* bf16 [n_layers, max_batch, n_heads, head_dim] */
+  void* k_store;              /* bf16 [n_layers, num_slots, n_kv_heads, head_dim] */
+  void* v_store;
+  const void* k_new;          /* bf16 [n_layers, max_batch, n_kv_heads, head_dim]:
+                                 the new tokens' rows, appended in the attention
+                                 launch; NULL (with v_new) for no append        */
+  const void* v_new;
+  void* out;                  /* bf16 [n_layers, max_batch, n_heads, head_dim] */
+  float scale;
+} pd_step_buffers;
+
+typedef struct pd_graph_pool pd_graph_pool;
+
+enum { PD_POOL_EAGER = 1 };   /* capture nothing: every key runs eagerly       */
+
+/* A pool over the handle's workspace.  Keys are 1, 2, 4, ... below max_batch,
+ * and max_batch; key k uses S = paged_decode_num_splits(k, 0).  Holds the
+ * pointers (the buffers must outlive the pool) and one private capture stream.
+ * No device memory is allocated. */
+pd_status paged_decode_graph_pool_create(pd_handle* h, const pd_step_buffers* bufs, uint32_t flags,
+                                         pd_graph_pool** out);
+
+/* Captures the step of every key:
+ *   steady bind, then per layer l: attention (append_attn with k_new/v_new
+ *   layer l, else attn) of q layer l, and the merge into out layer l.
+ * Capture executes nothing, so the buffers are not touched.  A key whose
+ * capture or instantiation fails runs eagerly afterwards (see _key). */
+pd_status paged_decode_graph_pool_warmup(pd_graph_pool* p);
+
+/* One steady decode step of requests 0 .. batch-1 (1 <= batch <= max_batch) on
+ * `stream`: writes `batch` into the workspace's active-request word, then
+ * replays (or runs eagerly) the step of the smallest key >= batch.  Every
+ * kernel stops at `batch` requests: the padding requests batch .. key-1 keep
+ * their lengths and their output rows.  The results equal those of the eager
+ * calls with the same batch and the key's split count, bit for bit. */
+pd_status paged_decode_graph_pool_step(pd_graph_pool* p, int32_t batch, hipStream_t stream);
+
+pd_status paged_decode_graph_pool_num_keys(const pd_graph_pool* p, int32_t* n_keys);
+/* Key `index`: its batch size, split count and whether it replays a graph. */
+pd_status paged_decode_graph_pool_key(const pd_graph_pool* p, int32_t index, int32_t* key, int32_t* num_splits,
+                                      int32_t* is_graph);
+/* Destroys the graphs and the capture stream (not the buffers). */
+pd_status paged_decode_graph_pool_destroy(pd_graph_pool* p);
+
 /* Diagnostics, never in the hot path: synchronises `stream`, returns the
  * device error word (PD_ERR_* bits) and clears it. */
 pd_status paged_decode_read_error(pd_handle* h, uint32_t* flags, hipStream_t stream);

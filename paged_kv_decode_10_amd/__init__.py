@@ -35,7 +35,7 @@ from ._abi import (  # noqa: F401
     PagedDecodeError,
 )
 
-__all__ = ["Config", "PagedDecode", "PagedDecodeError", "PD_BIND_FULL", "PD_BIND_STEADY",
+__all__ = ["Config", "PagedDecode", "GraphPool", "PagedDecodeError", "PD_BIND_FULL", "PD_BIND_STEADY",
            "workspace_bytes", "library_path"]
 
 
@@ -224,6 +224,76 @@ class PagedDecode:
         if getattr(self, "_h", None):
             _abi.lib().paged_decode_destroy(self._h)
             self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class GraphPool:
+    """Batch-size graph pool over a workspace (``paged_decode_graph_pool_*``).
+
+    The tensors are the caller's fixed step buffers, each sized for the
+    workspace's max_batch (see ``pd_step_buffers``); the pool keeps references
+    to them.  ``step(batch)`` runs one steady decode step of requests
+    0 .. batch-1 through the smallest captured key >= batch.
+    """
+
+    def __init__(self, ws: PagedDecode, *, seq_lens, position_ids, q, k_store, v_store, out, scale,
+                 req_to_page=None, req_base=None, k_new=None, v_new=None, eager=False):
+        c = ws.cfg
+        nb = c.max_batch
+        store_numel = c.n_layers * c.num_slots * c.n_kv_heads * c.head_dim
+        per_layer = c.n_layers * nb * c.n_heads * c.head_dim
+        new_numel = c.n_layers * nb * c.n_kv_heads * c.head_dim
+        b = _abi.PdStepBuffers()
+        b.seq_lens = _dev_ptr(seq_lens, torch.int32, "seq_lens", nb)
+        b.position_ids = _dev_ptr(position_ids, torch.int32, "position_ids", nb)
+        b.req_to_page = None if req_to_page is None else _dev_ptr(req_to_page, torch.int32, "req_to_page",
+                                                                   nb * c.max_pages_per_req)
+        b.req_base = None if req_base is None else _dev_ptr(req_base, torch.int32, "req_base", nb)
+        b.q = _dev_ptr(q, torch.bfloat16, "q", per_layer)
+        b.k_store = _dev_ptr(k_store, torch.bfloat16, "k_store", store_numel)
+        b.v_store = _dev_ptr(v_store, torch.bfloat16, "v_store", store_numel)
+        b.k_new = None if k_new is None else _dev_ptr(k_new, torch.bfloat16, "k_new", new_numel)
+        b.v_new = None if v_new is None else _dev_ptr(v_new, torch.bfloat16, "v_new", new_numel)
+        b.out = _dev_ptr(out, torch.bfloat16, "out", per_layer)
+        b.scale = float(scale)
+        self.ws = ws
+        self._keep = (seq_lens, position_ids, req_to_page, req_base, q, k_store, v_store, k_new, v_new, out)
+        self._buf = b
+        h = ctypes.c_void_p()
+        _abi.check("paged_decode_graph_pool_create",
+                   _abi.lib().paged_decode_graph_pool_create(ws._h, ctypes.byref(b),
+                                                             _abi.PD_POOL_EAGER if eager else 0, ctypes.byref(h)))
+        self._p = h
+
+    def warmup(self) -> None:
+        _abi.check("paged_decode_graph_pool_warmup", _abi.lib().paged_decode_graph_pool_warmup(self._p))
+
+    def step(self, batch: int, stream=None) -> None:
+        _abi.check("paged_decode_graph_pool_step",
+                   _abi.lib().paged_decode_graph_pool_step(self._p, batch, _stream_ptr(stream)))
+
+    def keys(self):
+        """[(key, num_splits, replays_a_graph)] for every key."""
+        L = _abi.lib()
+        n = ctypes.c_int32(0)
+        _abi.check("paged_decode_graph_pool_num_keys", L.paged_decode_graph_pool_num_keys(self._p, ctypes.byref(n)))
+        out = []
+        for i in range(n.value):
+            k, s, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+            _abi.check("paged_decode_graph_pool_key",
+                       L.paged_decode_graph_pool_key(self._p, i, ctypes.byref(k), ctypes.byref(s), ctypes.byref(g)))
+            out.append((k.value, s.value, bool(g.value)))
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_p", None):
+            _abi.lib().paged_decode_graph_pool_destroy(self._p)
+            self._p = None
 
     def __del__(self):
         try:

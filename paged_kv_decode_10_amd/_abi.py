@@ -31,6 +31,12 @@ EXPORTS = (
     "paged_decode_append_kv",
     "paged_decode_append_attn",
     "paged_decode_merge",
+    "paged_decode_graph_pool_create",
+    "paged_decode_graph_pool_warmup",
+    "paged_decode_graph_pool_step",
+    "paged_decode_graph_pool_num_keys",
+    "paged_decode_graph_pool_key",
+    "paged_decode_graph_pool_destroy",
     "paged_decode_read_error",
     "paged_decode_destroy",
     "paged_decode_strerror",
@@ -55,6 +61,25 @@ class PdConfig(ctypes.Structure):
 class PdLayout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_size_t) for name in (
         "arena_bytes", "kv_indptr", "kv_indices", "page_indptr", "o_part", "ml_part", "meta", "error_word")]
+
+
+class PdStepBuffers(ctypes.Structure):
+    _fields_ = [
+        ("seq_lens", ctypes.c_void_p),
+        ("position_ids", ctypes.c_void_p),
+        ("req_to_page", ctypes.c_void_p),
+        ("req_base", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("k_store", ctypes.c_void_p),
+        ("v_store", ctypes.c_void_p),
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+    ]
+
+
+PD_POOL_EAGER = 1
 
 
 class PagedDecodeError(RuntimeError):
@@ -88,6 +113,12 @@ def lib() -> ctypes.CDLL:
         "paged_decode_append_kv": [P, I32, I32, P, P, P, P, P],
         "paged_decode_append_attn": [P, I32, I32, I32, P, P, P, P, P, F, P],
         "paged_decode_merge": [P, I32, I32, P, P],
+        "paged_decode_graph_pool_create": [P, ctypes.POINTER(PdStepBuffers), ctypes.c_uint32, ctypes.POINTER(P)],
+        "paged_decode_graph_pool_warmup": [P],
+        "paged_decode_graph_pool_step": [P, I32, P],
+        "paged_decode_graph_pool_num_keys": [P, ctypes.POINTER(I32)],
+        "paged_decode_graph_pool_key": [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)],
+        "paged_decode_graph_pool_destroy": [P],
         "paged_decode_read_error": [P, ctypes.POINTER(ctypes.c_uint32), P],
         "paged_decode_destroy": [P],
     }

@@ -18,6 +18,7 @@ constexpr int kAppendThreads = 256;
 
 __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   const int b = blockIdx.x;
+  if (b >= active_batch(a.active, a.batch)) return;
   const int32_t end = a.kv_indptr[b + 1];
   if (end == a.kv_indptr[b]) return;
   const int64_t slot = a.kv_indices[end - 1];

@@ -271,7 +271,9 @@ split_attn_kernel(AttnArgs a) {
   const int tm = __builtin_amdgcn_readfirstlane(blockIdx.x * (kWaves / T) + wave / T);
   const int member = __builtin_amdgcn_readfirstlane(wave % T);
   const int r = lane >> 4, c = lane & 15;
-  const int B = a.batch, Hkv = a.n_kv_heads, S = a.num_splits, H = a.n_heads;
+  const int Hkv = a.n_kv_heads, S = a.num_splits, H = a.n_heads;
+  const int Bk = a.batch;  // launch batch: bounds the per-lane index loads below
+  const int B = active_batch(a.active, a.batch);
   const int Hs = Hkv / T, nch = kSplitChunks / T;
   PD_STAMP(0, wall_clock64());
 
@@ -287,7 +289,7 @@ split_attn_kernel(AttnArgs a) {
   pr.done = 0;
   const bool row_mode = S == 1;
   pr.row_mode = row_mode;
-  const int i_lane = lane <= B ? lane : B;
+  const int i_lane = lane <= Bk ? lane : Bk;  // entries past B are never used
   const int32_t pi_lane = a.page_indptr[i_lane];
   const int32_t ki_lane = a.kv_indptr[i_lane];
   const int32_t total_pages = a.meta[kMetaTotalPages];

@@ -37,9 +37,10 @@ bind_scan_kernel(BindArgs a) {
   __shared__ int wave_maxp[kScanThreads / 64];
   const int b = threadIdx.x;
   const int lane = b & 63, wave = b >> 6;
+  const int B = active_batch(a.active, a.batch);
   uint32_t flags = 0;
   int64_t len = 0;
-  if (b < a.batch) {
+  if (b < B) {
     int32_t L = a.seq_lens[b];
     if (a.mode == PD_BIND_STEADY) {
       L += 1;
@@ -62,10 +63,10 @@ bind_scan_kernel(BindArgs a) {
   // Clip to the kv_indices capacity so every later read stays in bounds.
   const int64_t lo = min(excl, a.max_total_tokens);
   const int64_t hi = min(excl + len, a.max_total_tokens);
-  if (b < a.batch && hi - lo < len) flags |= PD_ERR_TOTAL_OVER_CAP;
-  if (b == a.batch - 1) a.meta[kMetaTotalTokens] = (int32_t)hi;
-  const int pages = (b < a.batch) ? (int)((hi - lo + a.page_size - 1) / a.page_size) : 0;
-  if (b < a.batch) {
+  if (b < B && hi - lo < len) flags |= PD_ERR_TOTAL_OVER_CAP;
+  if (b == B - 1) a.meta[kMetaTotalTokens] = (int32_t)hi;
+  const int pages = (b < B) ? (int)((hi - lo + a.page_size - 1) / a.page_size) : 0;
+  if (b < B) {
     a.kv_indptr[b + 1] = (int32_t)hi;
     if (b == 0) a.kv_indptr[0] = 0;
   }
@@ -78,7 +79,7 @@ bind_scan_kernel(BindArgs a) {
   __syncthreads();
   int64_t pbefore = 0;
   for (int w = 0; w < wave; ++w) pbefore += wave_tot[w];
-  if (b < a.batch) {
+  if (b < B) {
     a.page_indptr[b + 1] = (int32_t)(pbefore + pincl);
     if (b == 0) a.page_indptr[0] = 0;
   }
@@ -105,6 +106,7 @@ constexpr int kFillThreads = 256;
 __global__ void __launch_bounds__(kFillThreads)
 bind_fill_kernel(BindArgs a) {
   const int b = blockIdx.x;
+  if (b >= active_batch(a.active, a.batch)) return;
   const int32_t start = a.kv_indptr[b];
   const int32_t len = a.kv_indptr[b + 1] - start;
   uint32_t flags = 0;

@@ -62,7 +62,7 @@ merge_kernel(MergeArgs a) {
   constexpr int kBatch = 16;
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
-  if (item >= a.batch * a.n_heads) return;
+  if (item >= active_batch(a.active, a.batch) * a.n_heads) return;
   const int64_t base = (int64_t)item * a.max_splits;  // row of split 0
   const float* ml = a.ml_part + base * 2;
   const float* op = a.o_part + base * D;
@@ -151,6 +151,7 @@ merge_wide_kernel(MergeArgs a) {
   __shared__ float s_m[kWideWaves], s_w[kWideWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int item = blockIdx.x;
+  if (item >= active_batch(a.active, a.batch) * a.n_heads) return;  // whole workgroup
   const int64_t base = (int64_t)item * a.max_splits;
   const float* ml = a.ml_part + base * 2;
   const float* op = a.o_part + base * D;

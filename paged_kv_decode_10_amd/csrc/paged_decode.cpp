@@ -9,15 +9,7 @@
 #include <new>
 #include <string.h>
 
-#include "pd_internal.h"
-
-struct pd_handle {
-  pd_config cfg;
-  pd_layout lay;
-  char* arena;
-  int device;
-  int num_cus;
-};
+#include "pd_host.h"
 
 namespace {
 
@@ -70,14 +62,10 @@ pd_layout make_layout(const pd_config* c) {
   return l;
 }
 
-template <typename T>
-T* at(const pd_handle* h, size_t off) {
-  return reinterpret_cast<T*>(h->arena + off);
-}
-
-pd_status hip_status(hipError_t e) { return e == hipSuccess ? PD_OK : PD_E_HIP; }
-
 }  // namespace
+
+using pdh::at;
+using pdh::hip_status;
 
 extern "C" {
 
@@ -140,6 +128,13 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t req
     *num_splits = requested;
     return PD_OK;
   }
+  *num_splits = pdh::auto_splits(h, batch);
+  return PD_OK;
+}
+
+}  // extern "C"
+
+int32_t pdh::auto_splits(const pd_handle* h, int32_t batch) {
   // The plan cuts the page sequence into 2048 equal chunks when no row needs
   // more than S splits for it; rows average 2048 / (batch * n_kv_heads) chunks,
   // so allow about twice that.  More splits than pages buys nothing.
@@ -148,16 +143,12 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t req
   if (S > h->cfg.max_pages_per_req) S = h->cfg.max_pages_per_req;
   if (S > h->cfg.max_splits) S = h->cfg.max_splits;
   if (S < 2) S = h->cfg.max_splits >= 2 ? 2 : 1;
-  *num_splits = (int32_t)S;
-  return PD_OK;
+  return (int32_t)S;
 }
 
-}  // extern "C"
-
-namespace {
-
-pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens, int32_t* d_position_ids,
-                      const int32_t* d_req_to_page, const int32_t* d_req_base, hipStream_t stream) {
+pd_status pdh::bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
+                           int32_t* d_position_ids, const int32_t* d_req_to_page, const int32_t* d_req_base,
+                           const int32_t* d_active, hipStream_t stream) {
   if (!h || !d_seq_lens || (!d_req_to_page && !d_req_base) || batch < 1) return PD_E_INVALID;
   if (mode != PD_BIND_FULL && mode != PD_BIND_STEADY) return PD_E_INVALID;
   if (mode == PD_BIND_STEADY && !d_position_ids) return PD_E_INVALID;
@@ -165,7 +156,7 @@ pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_
       (d_req_base && !aligned(d_req_base, 4)) || (d_position_ids && !aligned(d_position_ids, 4)))
     return PD_E_INVALID;
   if (batch > h->cfg.max_batch) return PD_E_CAPACITY;
-  pd::BindArgs a;
+  pd::BindArgs a{};
   a.batch = batch;
   a.mode = mode;
   a.page_size = h->cfg.page_size;
@@ -177,6 +168,7 @@ pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_
   a.position_ids = d_position_ids;
   a.req_to_page = d_req_to_page;
   a.req_base = d_req_base;
+  a.active = d_active;
   a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
   a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
   a.page_indptr = at<int32_t>(h, h->lay.page_indptr);
@@ -185,33 +177,29 @@ pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_
   return hip_status(pd::launch_bind(a, stream));
 }
 
-}  // namespace
-
 extern "C" {
 
 pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
                             int32_t* d_position_ids, const int32_t* d_req_to_page,
                             hipStream_t stream) {
   if (!d_req_to_page) return PD_E_INVALID;
-  return bind_launch(h, batch, mode, d_seq_lens, d_position_ids, d_req_to_page, nullptr, stream);
+  return pdh::bind_launch(h, batch, mode, d_seq_lens, d_position_ids, d_req_to_page, nullptr, nullptr, stream);
 }
 
 pd_status paged_decode_bind_contiguous(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
                                        int32_t* d_position_ids, const int32_t* d_req_base,
                                        hipStream_t stream) {
   if (!d_req_base) return PD_E_INVALID;
-  return bind_launch(h, batch, mode, d_seq_lens, d_position_ids, nullptr, d_req_base, stream);
+  return pdh::bind_launch(h, batch, mode, d_seq_lens, d_position_ids, nullptr, d_req_base, nullptr, stream);
 }
 
 }  // extern "C"
 
-namespace {
-
 // Shared by paged_decode_attn and paged_decode_append_attn (k_new == nullptr:
-// no append).
-pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
-                      const void* d_k_new, const void* d_v_new, const void* d_k_store,
-                      const void* d_v_store, float scale, hipStream_t stream) {
+// no append) and the graph pool.
+pd_status pdh::attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
+                           const void* d_k_new, const void* d_v_new, const void* d_k_store,
+                           const void* d_v_store, float scale, const int32_t* d_active, hipStream_t stream) {
   if (!h || !d_q || !d_k_store || !d_v_store || batch < 1 || num_splits < 1 || layer < 0)
     return PD_E_INVALID;
   if (!aligned(d_q, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16))
@@ -221,7 +209,7 @@ pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_sp
   if (batch > c.max_batch || num_splits > c.max_splits || layer >= c.n_layers)
     return PD_E_CAPACITY;
   const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
-  pd::AttnArgs a;
+  pd::AttnArgs a{};
   a.batch = batch;
   a.n_heads = c.n_heads;
   a.n_kv_heads = c.n_kv_heads;
@@ -244,24 +232,25 @@ pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_sp
   a.v_new = static_cast<const uint16_t*>(d_v_new);
   a.k_dst = const_cast<uint16_t*>(a.k_layer);
   a.v_dst = const_cast<uint16_t*>(a.v_layer);
+  a.active = d_active;
   return hip_status(pd::launch_attn(a, c.head_dim, stream));
 }
-
-}  // namespace
 
 extern "C" {
 
 pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
                             const void* d_q, const void* d_k_store, const void* d_v_store,
                             float scale, hipStream_t stream) {
-  return attn_launch(h, batch, layer, num_splits, d_q, nullptr, nullptr, d_k_store, d_v_store, scale, stream);
+  return pdh::attn_launch(h, batch, layer, num_splits, d_q, nullptr, nullptr, d_k_store, d_v_store, scale,
+                          nullptr, stream);
 }
 
 pd_status paged_decode_append_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
                                    const void* d_q, const void* d_k_new, const void* d_v_new,
                                    void* d_k_store, void* d_v_store, float scale, hipStream_t stream) {
   if (!d_k_new || !d_v_new) return PD_E_INVALID;
-  return attn_launch(h, batch, layer, num_splits, d_q, d_k_new, d_v_new, d_k_store, d_v_store, scale, stream);
+  return pdh::attn_launch(h, batch, layer, num_splits, d_q, d_k_new, d_v_new, d_k_store, d_v_store, scale,
+                          nullptr, stream);
 }
 
 pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, const void* d_k_new,
@@ -272,7 +261,7 @@ pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, con
   const pd_config& c = h->cfg;
   if (batch > c.max_batch || layer >= c.n_layers) return PD_E_CAPACITY;
   const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
-  pd::AppendArgs a;
+  pd::AppendArgs a{};
   a.batch = batch;
   a.row_bytes = c.n_kv_heads * c.head_dim * 2;
   a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
@@ -286,18 +275,7 @@ pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, con
 
 pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
                              hipStream_t stream) {
-  if (!h || !d_out || batch < 1 || num_splits < 1) return PD_E_INVALID;
-  if (!aligned(d_out, 16)) return PD_E_INVALID;
-  if (batch > h->cfg.max_batch || num_splits > h->cfg.max_splits) return PD_E_CAPACITY;
-  pd::MergeArgs a;
-  a.batch = batch;
-  a.n_heads = h->cfg.n_heads;
-  a.num_splits = num_splits;
-  a.max_splits = h->cfg.max_splits;
-  a.o_part = at<float>(h, h->lay.o_part);
-  a.ml_part = at<float>(h, h->lay.ml_part);
-  a.out = static_cast<uint16_t*>(d_out);
-  return hip_status(pd::launch_merge(a, h->cfg.head_dim, stream));
+  return pdh::merge_launch(h, batch, num_splits, d_out, nullptr, stream);
 }
 
 pd_status paged_decode_read_error(pd_handle* h, uint32_t* flags, hipStream_t stream) {
@@ -331,3 +309,20 @@ const char* paged_decode_strerror(int status) {
 }
 
 }  // extern "C"
+
+pd_status pdh::merge_launch(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out, const int32_t* d_active,
+                            hipStream_t stream) {
+  if (!h || !d_out || batch < 1 || num_splits < 1) return PD_E_INVALID;
+  if (!aligned(d_out, 16)) return PD_E_INVALID;
+  if (batch > h->cfg.max_batch || num_splits > h->cfg.max_splits) return PD_E_CAPACITY;
+  pd::MergeArgs a{};
+  a.batch = batch;
+  a.active = d_active;
+  a.n_heads = h->cfg.n_heads;
+  a.num_splits = num_splits;
+  a.max_splits = h->cfg.max_splits;
+  a.o_part = at<float>(h, h->lay.o_part);
+  a.ml_part = at<float>(h, h->lay.ml_part);
+  a.out = static_cast<uint16_t*>(d_out);
+  return hip_status(pd::launch_merge(a, h->cfg.head_dim, stream));
+}

@@ -1,0 +1,38 @@
+// Host-side internals shared by the C ABI (paged_decode.cpp) and the graph
+// pool (graph_pool.cpp): the handle and the launch helpers, which also take the
+// graph pool's active-request word (null outside the pool).
+#pragma once
+
+#include "pd_internal.h"
+
+struct pd_handle {
+  pd_config cfg;
+  pd_layout lay;
+  char* arena;
+  int device;
+  int num_cus;
+};
+
+namespace pdh {
+
+template <typename T>
+T* at(const pd_handle* h, size_t off) {
+  return reinterpret_cast<T*>(h->arena + off);
+}
+
+inline pd_status hip_status(hipError_t e) { return e == hipSuccess ? PD_OK : PD_E_HIP; }
+
+int32_t auto_splits(const pd_handle* h, int32_t batch);
+
+pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens, int32_t* d_position_ids,
+                      const int32_t* d_req_to_page, const int32_t* d_req_base, const int32_t* d_active,
+                      hipStream_t stream);
+
+pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
+                      const void* d_k_new, const void* d_v_new, const void* d_k_store, const void* d_v_store,
+                      float scale, const int32_t* d_active, hipStream_t stream);
+
+pd_status merge_launch(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out, const int32_t* d_active,
+                       hipStream_t stream);
+
+}  // namespace pdh

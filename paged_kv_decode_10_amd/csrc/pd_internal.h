@@ -14,6 +14,7 @@ enum MetaWord : int {
   kMetaMaxPages = 0,     // max over requests of ceil(L_b / page_size)
   kMetaTotalTokens = 1,  // sum of the (clamped) lengths
   kMetaTotalPages = 2,   // sum over requests of ceil(L_b / page_size)
+  kMetaActive = 4,       // active requests of a padded graph-pool step (graph pool only)
 };
 
 // The attention launches this many waves.  They work in teams of
@@ -27,8 +28,18 @@ inline __host__ __device__ int kv_team(int n_kv_heads) {
   return (n_kv_heads % 4 == 0) ? 4 : (n_kv_heads % 2 == 0) ? 2 : 1;
 }
 
+// Requests a kernel works on: `batch`, or in a graph-pool step (captured at a
+// padded batch) the active count the pool wrote into the arena, clamped to
+// [1, batch].  Requests past it are left untouched.
+__device__ __forceinline__ int active_batch(const int32_t* active, int batch) {
+  if (active == nullptr) return batch;
+  const int n = *active;
+  return n < 1 ? 1 : (n > batch ? batch : n);
+}
+
 struct BindArgs {
   int32_t batch;
+  const int32_t* active;      // null, or the graph pool's active-request word
   int32_t mode;
   int32_t page_size;
   int32_t max_pages_per_req;
@@ -48,6 +59,7 @@ struct BindArgs {
 
 struct AttnArgs {
   int32_t batch;
+  const int32_t* active;
   int32_t n_heads;
   int32_t n_kv_heads;
   int32_t group;              // n_heads / n_kv_heads
@@ -76,6 +88,7 @@ struct AttnArgs {
 
 struct MergeArgs {
   int32_t batch;
+  const int32_t* active;
   int32_t n_heads;
   int32_t num_splits;
   int32_t max_splits;
@@ -86,6 +99,7 @@ struct MergeArgs {
 
 struct AppendArgs {
   int32_t batch;
+  const int32_t* active;
   int32_t row_bytes;          // n_kv_heads * head_dim * 2
   const int32_t* kv_indptr;
   const int32_t* kv_indices;

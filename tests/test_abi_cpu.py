@@ -84,6 +84,10 @@ def test_host_side_rejections(abi):
     assert L.paged_decode_merge(None, 1, 1, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_kv(None, 1, 0, None, None, None, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_attn(None, 1, 0, 1, None, None, None, None, None, 1.0, None) == abi.PD_E_INVALID
+    assert L.paged_decode_graph_pool_create(None, None, 0, ctypes.byref(h)) == abi.PD_E_INVALID
+    assert L.paged_decode_graph_pool_warmup(None) == abi.PD_E_INVALID
+    assert L.paged_decode_graph_pool_step(None, 1, None) == abi.PD_E_INVALID
+    assert L.paged_decode_graph_pool_destroy(None) == abi.PD_E_INVALID
     assert L.paged_decode_destroy(None) == abi.PD_E_INVALID
     for code in range(5):
         assert L.paged_decode_strerror(code)

@@ -1,0 +1,111 @@
+"""GPU: the batch-size graph pool (paged_decode_graph_pool_*).
+
+Every step of the pool must equal, bit for bit, the eager calls at the same
+batch with the key's split count, and leave the padding requests (batch ..
+key-1) untouched.  A pool forced to run eagerly must give the same bits.
+"""
+import pytest
+import torch
+
+import workloads
+from paged_kv_decode_10_amd import PD_BIND_FULL, PD_BIND_STEADY, GraphPool
+from tests.gpu_harness import make_ws, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 7.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16)
+
+
+def _workload(layout="paged"):
+    return workloads.make_custom("pool", seed=80, n_layers=2,
+                                 seq_lens=lambda g: torch.randint(1, 700, (6,), generator=g).tolist(),
+                                 n_heads=16, n_kv_heads=4, head_dim=128, page_size=16, growth=12, layout=layout)
+
+
+def _new_rows(w, seed=9):
+    g = torch.Generator().manual_seed(seed)
+    shape = (w.n_layers, w.batch, w.n_kv_heads, w.head_dim)
+    return (torch.randn(shape, generator=g).to(torch.bfloat16).cuda(),
+            torch.randn(shape, generator=g).to(torch.bfloat16).cuda())
+
+
+class _State:
+    def __init__(self, w, append, layout):
+        self.w = w
+        self.dev = to_device(w)
+        self.ws = make_ws(w)
+        self.out = torch.full((w.n_layers, w.batch, w.n_heads, w.head_dim), SENTINEL, dtype=torch.bfloat16,
+                              device="cuda")
+        self.kn, self.vn = _new_rows(w) if append else (None, None)
+        self.base = w.meta["req_base"].cuda() if layout == "contiguous" else None
+        self.bind(w.batch, PD_BIND_FULL)
+
+    def bind(self, B, mode):
+        d = self.dev
+        if self.base is not None:
+            self.ws.bind_contiguous(B, mode, d.seq_lens, d.position_ids, self.base)
+        else:
+            self.ws.bind(B, mode, d.seq_lens, d.position_ids, d.req_to_page)
+
+    def eager_step(self, B, S):
+        w, d = self.w, self.dev
+        self.bind(B, PD_BIND_STEADY)
+        for l in range(w.n_layers):
+            if self.kn is not None:
+                self.ws.append_attn(B, l, S, d.q[l][:B], self.kn[l][:B], self.vn[l][:B], d.k, d.v, w.scale)
+            else:
+                self.ws.attn(B, l, S, d.q[l][:B], d.k, d.v, w.scale)
+            self.ws.merge(B, S, self.out[l][:B])
+
+    def pool(self, eager=False):
+        d = self.dev
+        return GraphPool(self.ws, seq_lens=d.seq_lens, position_ids=d.position_ids, q=d.q, k_store=d.k,
+                         v_store=d.v, out=self.out, scale=self.w.scale,
+                         req_to_page=None if self.base is not None else d.req_to_page, req_base=self.base,
+                         k_new=self.kn, v_new=self.vn, eager=eager)
+
+
+@pytest.mark.parametrize("append,layout", [(False, "paged"), (True, "paged"), (True, "contiguous")])
+def test_pool_steps_match_eager(append, layout):
+    say(f"[pool] append={append} layout={layout}")
+    w = _workload(layout)
+    ref, got, eag = _State(w, append, layout), _State(w, append, layout), _State(w, append, layout)
+    pool = got.pool()
+    pool.warmup()
+    keys = pool.keys()
+    assert [k for k, _, _ in keys] == [1, 2, 4, 6]
+    assert all(g for _, _, g in keys), keys
+    eager_pool = eag.pool(eager=True)
+    eager_pool.warmup()
+    assert not any(g for _, _, g in eager_pool.keys())
+    split_of = {k: s for k, s, _ in keys}
+    for B in (6, 3, 3, 1, 4, 2, 5):
+        key = min(k for k in split_of if k >= B)
+        seq_before = got.dev.seq_lens.clone()
+        out_before = got.out.clone()
+        ref.eager_step(B, split_of[key])
+        a0 = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+        pool.step(B)
+        eager_pool.step(B)
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_stats().get("allocation.all.allocated", 0) == a0, "the pool step allocated"
+        for s in (got, eag):
+            assert torch.equal(_bits(s.out[:, :B]), _bits(ref.out[:, :B])), f"B={B} key={key}"
+            assert torch.equal(_bits(s.out[:, B:]), _bits(out_before[:, B:])), "padding outputs were written"
+            assert torch.equal(s.dev.seq_lens, ref.dev.seq_lens), "lengths differ"
+            assert torch.equal(_bits(s.dev.k), _bits(ref.dev.k)) and torch.equal(_bits(s.dev.v), _bits(ref.dev.v))
+        assert torch.equal(got.dev.seq_lens[B:], seq_before[B:]), "padding lengths were advanced"
+        assert torch.equal(got.dev.seq_lens[:B], seq_before[:B] + 1)
+    assert got.ws.read_error() == 0
+    pool.close()
+    eager_pool.close()
