@@ -200,6 +200,61 @@ def config_sweep(names, reps: int, oracle_budget: float):
     return rows
 
 
+def pool_sweep(batches, steps: int, warmup: int):
+    """Graph pool on the 24-layer step workload: per batch size, the step time
+    replaying the pool's captured graph vs the same pool run eagerly (every
+    kernel launched from the host), both HIP-event timed over `steps` steps."""
+    import torch
+
+    import workloads
+    from paged_kv_decode_10_amd import PD_BIND_FULL, Config, GraphPool, PagedDecode
+
+    growth = 2 * (steps + warmup) * len(batches) + 8
+    w = workloads.make("step", growth=growth)
+    B, H, Hkv, D, NL = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.n_layers
+    cfg = Config(n_layers=NL, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size, max_batch=B,
+                 max_splits=256, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
+                 max_total_tokens=int(w.seq_lens.sum()) + growth * B)
+    ws = PagedDecode(cfg)
+    seq, pos, tab = w.seq_lens.cuda(), w.position_ids.cuda(), w.req_to_page.cuda()
+    q, kst, vst = w.q.cuda(), w.k_store.cuda(), w.v_store.cuda()
+    out = torch.empty((NL, B, H, D), dtype=torch.bfloat16, device="cuda")
+    ws.bind(B, PD_BIND_FULL, seq, pos, tab)
+    pools = {}
+    for eager in (False, True):
+        pools[eager] = GraphPool(ws, seq_lens=seq, position_ids=pos, q=q, k_store=kst, v_store=vst, out=out,
+                                 scale=w.scale, req_to_page=tab, eager=eager)
+        pools[eager].warmup()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = []
+    for b in batches:
+        res = {}
+        for eager in (False, True):
+            p = pools[eager]
+            for _ in range(warmup):
+                p.step(b)
+            torch.cuda.synchronize()
+            L0 = seq[:b].to(torch.int64).clone()
+            e0.record()
+            for _ in range(steps):
+                p.step(b)
+            e1.record()
+            torch.cuda.synchronize()
+            kv = sum(int((L0 + i + 1).sum()) for i in range(steps)) * Hkv * D * 4 * NL
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            res[eager] = (us, kv / (us * 1e-6 * steps) / 1e9)
+        rows.append({"batch": b, "graph_us_per_step": round(res[False][0], 1),
+                     "eager_us_per_step": round(res[True][0], 1),
+                     "speedup": round(res[True][0] / res[False][0], 3),
+                     "graph_kv_gbs": round(res[False][1], 1)})
+        log(f"[pool] B={b}: graph {res[False][0]:.1f} us/step ({res[False][1]:.0f} GB/s KV), "
+            f"eager {res[True][0]:.1f} us/step -> x{res[True][0] / res[False][0]:.2f}")
+    keys = pools[False].keys()
+    for p in pools.values():
+        p.close()
+    return rows, keys
+
+
 def oracle_time(w, budget_s: float):
     """The oracle's decode attention on (request, kv head) pairs of the same
     inputs until about budget_s, scaled to KV bytes per second."""
@@ -237,6 +292,9 @@ def main() -> int:
                          "NAME@contiguous for the contiguous-cache layout) timed one launch at a time with the "
                          "caches flushed; prints one JSON line")
     ap.add_argument("--config-reps", type=int, default=20)
+    ap.add_argument("--pool", default="",
+                    help="instead of the step: comma-separated batch sizes run through the graph pool (replayed "
+                         "and eager) on the 24-layer step workload; prints one JSON line")
     ap.add_argument("--oracle-budget", type=float, default=0.0,
                     help="with --configs: seconds of oracle timing per config (0 = none)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
@@ -256,6 +314,12 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 2
+    if args.pool:
+        rows, keys = pool_sweep([int(x) for x in args.pool.split(",") if x], args.steps, args.warmup)
+        print(json.dumps({"metric": "graph pool: decode step time, replay vs eager", "unit": "us/step",
+                          "n_gpus": 1, "data": "synthetic", "dtype": "bf16", "keys": keys, "batches": rows}),
+              flush=True)
+        return 0
     if args.configs:
         rows = config_sweep([x for x in args.configs.split(",") if x], args.config_reps, args.oracle_budget)
         print(json.dumps({"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "data": "synthetic", "dtype": "bf16",
