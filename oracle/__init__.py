@@ -31,6 +31,8 @@ from .paged_attention import (  # noqa: F401
     kv_indices_contiguous,
     kv_indptr,
     merge_splits,
+    prefill_attention,
+    qo_indptr,
     SPLIT_CHUNKS,
     TEAM_MAX,
     chunk_pages,

@@ -190,6 +190,49 @@ def decode_attention(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale
 
 
 # --------------------------------------------------------------------------
+# Paged prefill / extend ([WS] / [CA] bullets on the prefill qo_indptr built
+# once per step in the workspace and reused by every layer's prefill).
+# Reading: request b's last n_b = extend_lens[b] cached tokens are new and each
+# has a query; q rows are laid out request after request (qo_indptr is the
+# exclusive prefix sum of extend_lens).  New token i of request b sits at
+# position L_b - n_b + i and attends causally: to cached tokens 0 .. that
+# position (the prefix and the new tokens up to itself).
+# --------------------------------------------------------------------------
+
+def qo_indptr(extend_lens) -> np.ndarray:
+    """Exclusive prefix sum of the new-token counts."""
+    return kv_indptr(extend_lens)
+
+
+def prefill_attention(q_rows, k_layer, v_layer, seq_lens, extend_lens, kv_ptr, indices, scale, n_kv_heads):
+    """Causal attention of every new token over its request's cache.
+
+    q_rows [sum n_b, H, D]; returns out [sum n_b, H, D] and lse [sum n_b, H]
+    (float64).
+    """
+    q = to_f64(q_rows)
+    T, H, D = q.shape
+    G = H // n_kv_heads
+    L = np.asarray(seq_lens).reshape(-1).astype(np.int64)
+    n = np.asarray(extend_lens).reshape(-1).astype(np.int64)
+    qo = qo_indptr(n)
+    out = np.full((T, H, D), np.nan)
+    lse = np.full((T, H), np.nan)
+    for b in range(len(L)):
+        slots = indices[kv_ptr[b]:kv_ptr[b + 1]]
+        for g in range(n_kv_heads):
+            K = gather_rows(k_layer[:, g], slots)
+            V = gather_rows(v_layer[:, g], slots)
+            for i in range(int(n[b])):
+                pos = int(L[b] - n[b] + i)      # this token's position
+                for h in range(g * G, (g + 1) * G):
+                    o, m, lnz = attention_rows(q[qo[b] + i, h], K[:pos + 1], V[:pos + 1], scale)
+                    out[qo[b] + i, h] = o
+                    lse[qo[b] + i, h] = m + lnz
+    return out, lse
+
+
+# --------------------------------------------------------------------------
 # Split-KV partials and their log-sum-exp merge ([WS] bullets on
 # decode_o_part / decode_ml_part and the split partial buffers).
 # --------------------------------------------------------------------------

@@ -441,3 +441,60 @@ def test_workload_shapes():
     owned = set(w.req_to_page[w.req_to_page >= 0].tolist())
     free = [p for p in range(w.num_pages) if p not in owned]
     assert free and torch.isnan(w.k_store[0, free[0] * 16]).all()
+
+
+# --------------------------------------------------------------- prefill ----
+
+def test_prefill_single_new_token_is_decode():
+    """n_b = 1 for every request: the newest token attends to all L_b tokens."""
+    w = workloads.make("tiny")
+    L = w.seq_lens.numpy()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    ref, ref_lse = oracle.decode_attention(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale, w.n_kv_heads)
+    out, lse = oracle.prefill_attention(w.q[0], w.k_store[0], w.v_store[0], L, [1] * w.batch, ip, ix, w.scale,
+                                        w.n_kv_heads)
+    assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("name", ["prefill_tiny"])
+def test_prefill_against_sdpa_with_causal_mask(name):
+    """torch's float64 SDPA over each request's dense K/V with a boolean mask
+    that lets query i see keys 0 .. L_b - n_b + i."""
+    w = workloads.make(name)
+    L = w.seq_lens.numpy()
+    n = w.meta["extend_lens"].numpy()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    out, lse = oracle.prefill_attention(w.q[0], w.k_store[0], w.v_store[0], L, n, ip, ix, w.scale, w.n_kv_heads)
+    G = w.group
+    row = 0
+    for b in range(w.batch):
+        # dense K/V of the request, built by walking its page list (not the oracle's gather)
+        slots = [int(w.req_to_page[b, t // w.page_size]) * w.page_size + t % w.page_size for t in range(L[b])]
+        K = w.k_store[0, slots].to(torch.float64).repeat_interleave(G, dim=1).transpose(0, 1)  # [H, L, D]
+        V = w.v_store[0, slots].to(torch.float64).repeat_interleave(G, dim=1).transpose(0, 1)
+        Q = w.q[0, row:row + n[b]].to(torch.float64).transpose(0, 1)  # [H, n, D]
+        mask = torch.arange(L[b])[None, :] <= (L[b] - n[b] + torch.arange(n[b]))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=w.scale)
+        np.testing.assert_allclose(out[row:row + n[b]], ref.transpose(0, 1).numpy(), atol=1e-12, rtol=0)
+        s = w.scale * torch.einsum("hnd,hld->hnl", Q, K)
+        s = s.masked_fill(~mask, float("-inf"))
+        np.testing.assert_allclose(lse[row:row + n[b]], torch.logsumexp(s, -1).transpose(0, 1).numpy(),
+                                   atol=1e-12, rtol=0)
+        row += n[b]
+
+
+def test_prefill_first_token_of_a_fresh_prompt_is_its_value_row():
+    """No prefix: new token 0 sees only itself, so its output is its V row."""
+    w = workloads.make("prefill_tiny")
+    L = w.seq_lens.numpy()
+    n = w.meta["extend_lens"].numpy()
+    assert L[0] == n[0]
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    out, _ = oracle.prefill_attention(w.q[0], w.k_store[0], w.v_store[0], L, n, ip, ix, w.scale, w.n_kv_heads)
+    slot0 = int(w.req_to_page[0, 0]) * w.page_size
+    for h in range(w.n_heads):
+        assert np.array_equal(out[0, h], w.v_store[0, slot0, h // w.group].to(torch.float64).numpy())
+
+
+def test_qo_indptr():
+    assert oracle.qo_indptr([3, 0, 5]).tolist() == [0, 3, 3, 8]

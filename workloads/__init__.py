@@ -11,7 +11,8 @@ Layouts (all CPU torch tensors):
   position_ids  int32 [B]            (= seq_lens - 1: the position of the
                                       newest token, whose K/V is already stored)
   req_to_page   int32 [B, max_pages_per_req]   page ids, -1 where unused
-  q             bf16  [n_layers, B, n_heads, head_dim]
+  q             bf16  [n_layers, B, n_heads, head_dim]  (prefill workloads:
+                                      [n_layers, sum(extend_lens), n_heads, head_dim])
   k_store       bf16  [n_layers, num_slots, n_kv_heads, head_dim]
   v_store       bf16  [n_layers, num_slots, n_kv_heads, head_dim]
 Page p owns slots [p*page_size, (p+1)*page_size).  Pages that no request owns
@@ -28,7 +29,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "make", "make_custom", "CONFIGS"]
+__all__ = ["Workload", "make", "make_custom", "CONFIGS", "PREFILL_CONFIGS"]
 
 
 @dataclass
@@ -83,7 +84,7 @@ def _fill_store(gen, n_layers, num_slots, hkv, d, chunk_rows=1 << 16):
 def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim,
                 page_size=16, num_pages=None, pool_factor=1.25, growth=0,
                 max_pages_per_req=None, q_scale=1.0, scale=None,
-                nan_unassigned=True, shuffle=True, layout="paged"):
+                nan_unassigned=True, shuffle=True, layout="paged", extend_lens=None):
     """Build a workload.
 
     ``seq_lens`` is either a list of ints or a callable ``gen -> list`` that
@@ -96,10 +97,19 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
     max_pages_per_req pages instead (regions in a seeded random order, plus
     one spare region of NaN); ``meta["req_base"]`` holds each request's first
     slot, and ``req_to_page`` lists the region's pages in order.
+    ``extend_lens`` (a list or a callable ``(gen, lens) -> list``, drawn right
+    after the lengths) makes a prefill / extend workload: request b's last
+    extend_lens[b] tokens are new, and q holds one row per new token,
+    [n_layers, sum(extend_lens), n_heads, head_dim], request after request.
     """
     gen = torch.Generator().manual_seed(seed)
     lens = list(seq_lens(gen)) if callable(seq_lens) else list(seq_lens)
     B = len(lens)
+    ext = None
+    if extend_lens is not None:
+        ext = list(extend_lens(gen, lens)) if callable(extend_lens) else list(extend_lens)
+        if len(ext) != B or any(e < 0 or e > x for e, x in zip(ext, lens)):
+            raise ValueError("extend_lens must have one entry per request, 0 <= extend_lens[b] <= seq_lens[b]")
     pages_b = _pages_needed([x + growth for x in lens], page_size)
     if layout == "contiguous":
         mppr = max_pages_per_req if max_pages_per_req is not None else max(1, max(pages_b))
@@ -129,7 +139,8 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
     for b, pb in enumerate(pages_b):
         req_to_page[b, :pb] = perm[off:off + pb]
         off += pb
-    q = torch.randn((n_layers, B, n_heads, head_dim), generator=gen)
+    q_rows = B if ext is None else sum(ext)
+    q = torch.randn((n_layers, q_rows, n_heads, head_dim), generator=gen)
     if q_scale != 1.0:
         q = q * q_scale
     q = q.to(torch.bfloat16)
@@ -153,6 +164,7 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
                     seq_lens=seq, position_ids=(seq - 1).clamp(min=0), req_to_page=req_to_page,
                     q=q, k_store=k_store, v_store=v_store,
                     meta={"seed": seed, "growth": growth, "q_scale": q_scale, "layout": layout,
+                          "extend_lens": None if ext is None else torch.tensor(ext, dtype=torch.int32),
                           "req_base": (req_to_page[:, 0].to(torch.int32) * page_size if layout == "contiguous"
                                        else None)})
 
@@ -178,12 +190,31 @@ CONFIGS = {
 }
 
 
+def _extend_uniform(lo, hi):
+    """New tokens per request ~ U{lo..hi}, at most the request's length."""
+    def draw(gen, lens):
+        return [min(int(x), int(torch.randint(lo, hi + 1, (1,), generator=gen))) for x in lens]
+    return draw
+
+
+PREFILL_CONFIGS = {
+    # 2 requests: a fresh prompt (no prefix) and an extend over a 9-token prefix
+    "prefill_tiny": dict(seed=20, n_layers=1, seq_lens=[21, 40], extend_lens=[21, 31], n_heads=4,
+                         n_kv_heads=2, head_dim=64, page_size=16),
+    # extends: prefix ~U[0, 2048] plus U[64, 1024] new tokens, 4 requests
+    "prefill": dict(seed=21, n_layers=1, seq_lens=_uniform_lens(4, 64, 3072), extend_lens=_extend_uniform(64, 1024),
+                    n_heads=32, n_kv_heads=8, head_dim=128, page_size=16),
+}
+
+
 def make(name: str, **overrides) -> Workload:
     """Build a named workload; ``sweepN`` gives B=N requests of 4096 tokens."""
     if name.startswith("sweep"):
         B = int(name[5:])
         cfg = dict(seed=5, n_layers=1, seq_lens=[4096] * B, n_heads=32, n_kv_heads=8,
                    head_dim=128, page_size=16)
+    elif name in PREFILL_CONFIGS:
+        cfg = dict(PREFILL_CONFIGS[name])
     else:
         cfg = dict(CONFIGS[name])
     cfg.update(overrides)
