@@ -60,8 +60,10 @@ enum {
                                       clamped to that                          */
   PD_ERR_TOTAL_OVER_CAP = 1u << 2, /* sum(seq_lens) > max_total_tokens: the
                                       lengths are clipped to fit               */
-  PD_ERR_BAD_PAGE = 1u << 3        /* a page id outside [0, num_slots/page_size):
+  PD_ERR_BAD_PAGE = 1u << 3,       /* a page id outside [0, num_slots/page_size):
                                       its slots are redirected to slot 0       */
+  PD_ERR_EXTEND_OVER_LEN = 1u << 4 /* extend bind: extend_lens[b] > seq_lens[b]
+                                      (after clipping): treated as seq_lens[b] */
 };
 
 /* Bind modes ([CA]: steady-state detection lets bind increment seq_lens and
@@ -101,6 +103,10 @@ typedef struct pd_layout {
                          l = sum exp(s - m); lse = m + ln l; an empty split
                          holds (-inf, -inf) and its o_part row is
                          unspecified ([WS] decode_ml_part)                     */
+  size_t qo_indptr;   /* int32 [max_batch + 1]: extend bind: prefix sum of the
+                         new-token counts (prefill query rows)                 */
+  size_t item_indptr; /* int32 [max_batch + 1]: extend bind: prefix sum of the
+                         prefill work items per request                        */
   size_t meta;        /* int32 [16]: [0] = max pages of any request this step,
                          [1] = total tokens, [2] = total pages this step       */
   size_t error_word;  /* uint32: PD_ERR_* bits                                 */
@@ -202,6 +208,32 @@ pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, con
 pd_status paged_decode_append_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
                                    const void* d_q, const void* d_k_new, const void* d_v_new,
                                    void* d_k_store, void* d_v_store, float scale, hipStream_t stream);
+
+/* ---- Paged prefill / extend ([WS]/[CA]: the prefill qo_indptr is built once
+ * per step in the workspace and reused by every layer's prefill) ---- */
+
+/* Extend bind: request b holds L_b = d_seq_lens[b] cached tokens (K/V of all
+ * of them already in the stores), of which the last n_b = d_extend_lens[b]
+ * are new and have query rows.  Writes kv_indptr / kv_indices (as
+ * paged_decode_bind in PD_BIND_FULL mode, through d_req_to_page, or as
+ * paged_decode_bind_contiguous through d_req_base: exactly one non-NULL),
+ * qo_indptr = prefix sum of n_b, and the prefill work list.  n_b is clamped
+ * to [0, L_b] (PD_ERR_NEG_SEQ_LEN / PD_ERR_EXTEND_OVER_LEN). */
+pd_status paged_decode_bind_extend(pd_handle* h, int32_t batch, int32_t* d_seq_lens, const int32_t* d_extend_lens,
+                                   const int32_t* d_req_to_page, const int32_t* d_req_base, hipStream_t stream);
+
+/* Causal attention of every new token over its request's cache, one layer:
+ * new token i of request b (query row qo_indptr[b] + i, position
+ * p = L_b - n_b + i) attends to that request's tokens 0 .. p:
+ *   out[row, h, :] = sum_t softmax_t(scale * q[row, h] . K_t) V_t   (t <= p),
+ * kv head of query head h = h / (n_heads / n_kv_heads); rounded to bf16.
+ *   d_q    bf16 [sum n_b, n_heads, head_dim] (rows ragged by qo_indptr)
+ *   d_out  bf16 [sum n_b, n_heads, head_dim], caller-owned
+ *   stores as in paged_decode_attn.  Reads the last extend bind.  One
+ * persistent launch (2048 waves over (request, kv head, 16 query rows)). */
+pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q,
+                                    const void* d_k_store, const void* d_v_store, float scale, void* d_out,
+                                    hipStream_t stream);
 
 /* Log-sum-exp merge of the S partials into decode_out ([WS]: decode_out is
  * preallocated in the workspace):

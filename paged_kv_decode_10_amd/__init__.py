@@ -28,6 +28,7 @@ from ._abi import (  # noqa: F401
     PD_E_INVALID,
     PD_E_UNSUPPORTED,
     PD_ERR_BAD_PAGE,
+    PD_ERR_EXTEND_OVER_LEN,
     PD_ERR_NEG_SEQ_LEN,
     PD_ERR_SEQ_OVER_TABLE,
     PD_ERR_TOTAL_OVER_CAP,
@@ -207,6 +208,38 @@ class PagedDecode:
         _abi.check("paged_decode_append_attn",
                    _abi.lib().paged_decode_append_attn(self._h, batch, layer, num_splits, p_q, p_kn, p_vn, p_k,
                                                        p_v, float(scale), _stream_ptr(stream)))
+
+    def bind_extend(self, batch: int, seq_lens: torch.Tensor, extend_lens: torch.Tensor, req_to_page=None,
+                    req_base=None, stream=None) -> None:
+        """Extend / prefill bind: the last extend_lens[b] of seq_lens[b] tokens are new (query rows)."""
+        c = self.cfg
+        p_sl = _dev_ptr(seq_lens, torch.int32, "seq_lens", batch)
+        p_ext = _dev_ptr(extend_lens, torch.int32, "extend_lens", batch)
+        p_tab = None if req_to_page is None else _dev_ptr(req_to_page, torch.int32, "req_to_page",
+                                                           batch * c.max_pages_per_req)
+        p_base = None if req_base is None else _dev_ptr(req_base, torch.int32, "req_base", batch)
+        _abi.check("paged_decode_bind_extend",
+                   _abi.lib().paged_decode_bind_extend(self._h, batch, p_sl, p_ext, p_tab, p_base,
+                                                       _stream_ptr(stream)))
+
+    def prefill_attn(self, batch: int, layer: int, q: torch.Tensor, k_store: torch.Tensor, v_store: torch.Tensor,
+                     scale: float, out: torch.Tensor, stream=None) -> None:
+        """Causal attention of the new tokens of the last extend bind (q, out: [rows, n_heads, head_dim])."""
+        c = self.cfg
+        store_numel = c.n_layers * c.num_slots * c.n_kv_heads * c.head_dim
+        if q.dim() != 3 or q.shape[1:] != (c.n_heads, c.head_dim) or out.shape != q.shape:
+            raise ValueError("q and out must be [rows, n_heads, head_dim] with the same shape")
+        p_q = _dev_ptr(q, torch.bfloat16, "q")
+        p_o = _dev_ptr(out, torch.bfloat16, "out")
+        p_k = _dev_ptr(k_store, torch.bfloat16, "k_store", store_numel)
+        p_v = _dev_ptr(v_store, torch.bfloat16, "v_store", store_numel)
+        _abi.check("paged_decode_prefill_attn",
+                   _abi.lib().paged_decode_prefill_attn(self._h, batch, layer, p_q, p_k, p_v, float(scale), p_o,
+                                                        _stream_ptr(stream)))
+
+    @property
+    def qo_indptr(self):
+        return self._view(self.layout["qo_indptr"], torch.int32, (self.cfg.max_batch + 1,))
 
     def merge(self, batch: int, num_splits: int, out: torch.Tensor, stream=None) -> None:
         c = self.cfg

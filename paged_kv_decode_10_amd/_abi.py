@@ -19,6 +19,7 @@ PD_ERR_NEG_SEQ_LEN = 1 << 0
 PD_ERR_SEQ_OVER_TABLE = 1 << 1
 PD_ERR_TOTAL_OVER_CAP = 1 << 2
 PD_ERR_BAD_PAGE = 1 << 3
+PD_ERR_EXTEND_OVER_LEN = 1 << 4
 
 EXPORTS = (
     "paged_decode_workspace_bytes",
@@ -31,6 +32,8 @@ EXPORTS = (
     "paged_decode_append_kv",
     "paged_decode_append_attn",
     "paged_decode_merge",
+    "paged_decode_bind_extend",
+    "paged_decode_prefill_attn",
     "paged_decode_graph_pool_create",
     "paged_decode_graph_pool_warmup",
     "paged_decode_graph_pool_step",
@@ -60,7 +63,8 @@ class PdConfig(ctypes.Structure):
 
 class PdLayout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_size_t) for name in (
-        "arena_bytes", "kv_indptr", "kv_indices", "page_indptr", "o_part", "ml_part", "meta", "error_word")]
+        "arena_bytes", "kv_indptr", "kv_indices", "page_indptr", "o_part", "ml_part", "qo_indptr", "item_indptr",
+        "meta", "error_word")]
 
 
 class PdStepBuffers(ctypes.Structure):
@@ -113,6 +117,8 @@ def lib() -> ctypes.CDLL:
         "paged_decode_append_kv": [P, I32, I32, P, P, P, P, P],
         "paged_decode_append_attn": [P, I32, I32, I32, P, P, P, P, P, F, P],
         "paged_decode_merge": [P, I32, I32, P, P],
+        "paged_decode_bind_extend": [P, I32, P, P, P, P, P],
+        "paged_decode_prefill_attn": [P, I32, I32, P, P, P, F, P, P],
         "paged_decode_graph_pool_create": [P, ctypes.POINTER(PdStepBuffers), ctypes.c_uint32, ctypes.POINTER(P)],
         "paged_decode_graph_pool_warmup": [P],
         "paged_decode_graph_pool_step": [P, I32, P],

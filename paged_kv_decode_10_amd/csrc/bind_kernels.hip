@@ -93,6 +93,42 @@ bind_scan_kernel(BindArgs a) {
     a.meta[kMetaMaxPages] = m;
     a.meta[kMetaTotalPages] = (int32_t)ptotal;
   }
+  if (a.extend_lens != nullptr) {
+    // Extend / prefill: the last n_b of the (clipped) tokens are new, one
+    // query row each; qo_indptr is the prefix sum of n_b, and item_indptr that
+    // of the work items n_kv_heads * ceil(n_b * group / 16).
+    int64_t nb = 0;
+    if (b < B) {
+      nb = a.extend_lens[b];
+      if (nb < 0) { nb = 0; flags |= PD_ERR_NEG_SEQ_LEN; }
+      if (nb > hi - lo) { nb = hi - lo; flags |= PD_ERR_EXTEND_OVER_LEN; }
+    }
+    const int64_t items = (int64_t)a.n_kv_heads * ((nb * a.group + 15) / 16);
+    const int64_t qincl = wave_inclusive_scan(nb);
+    const int64_t iincl = wave_inclusive_scan(items);
+    __syncthreads();  // wave_tot is reused
+    if (lane == 63) wave_tot[wave] = qincl;
+    __syncthreads();
+    int64_t qbefore = 0;
+    for (int w = 0; w < wave; ++w) qbefore += wave_tot[w];
+    __syncthreads();
+    if (lane == 63) wave_tot[wave] = iincl;
+    __syncthreads();
+    int64_t ibefore = 0;
+    for (int w = 0; w < wave; ++w) ibefore += wave_tot[w];
+    if (b < B) {
+      a.qo_indptr[b + 1] = (int32_t)(qbefore + qincl);
+      a.item_indptr[b + 1] = (int32_t)(ibefore + iincl);
+      if (b == 0) {
+        a.qo_indptr[0] = 0;
+        a.item_indptr[0] = 0;
+      }
+      if (b == B - 1) {
+        a.meta[kMetaTotalQ] = (int32_t)(qbefore + qincl);
+        a.meta[kMetaTotalItems] = (int32_t)(ibefore + iincl);
+      }
+    }
+  }
   if (flags) atomicOr(a.error_word, flags);
 }
 

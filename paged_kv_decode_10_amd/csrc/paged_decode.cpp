@@ -54,6 +54,10 @@ pd_layout make_layout(const pd_config* c) {
   off = align_up(off + rows * c->head_dim * 4);
   l.ml_part = off;
   off = align_up(off + rows * 2 * 4);
+  l.qo_indptr = off;
+  off = align_up(off + (size_t)(c->max_batch + 1) * 4);
+  l.item_indptr = off;
+  off = align_up(off + (size_t)(c->max_batch + 1) * 4);
   l.meta = off;
   off = align_up(off + 16 * 4);
   l.error_word = off;
@@ -103,6 +107,8 @@ pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena, size_
   if (e == hipSuccess)
     e = hipMemsetAsync(h->arena + lay.page_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.meta, 0, 16 * 4, nullptr);
+  if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.qo_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
+  if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.item_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.error_word, 0, 4, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) {
@@ -148,7 +154,7 @@ int32_t pdh::auto_splits(const pd_handle* h, int32_t batch) {
 
 pd_status pdh::bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
                            int32_t* d_position_ids, const int32_t* d_req_to_page, const int32_t* d_req_base,
-                           const int32_t* d_active, hipStream_t stream) {
+                           const int32_t* d_active, hipStream_t stream, const int32_t* d_extend_lens) {
   if (!h || !d_seq_lens || (!d_req_to_page && !d_req_base) || batch < 1) return PD_E_INVALID;
   if (mode != PD_BIND_FULL && mode != PD_BIND_STEADY) return PD_E_INVALID;
   if (mode == PD_BIND_STEADY && !d_position_ids) return PD_E_INVALID;
@@ -174,6 +180,14 @@ pd_status pdh::bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d
   a.page_indptr = at<int32_t>(h, h->lay.page_indptr);
   a.meta = at<int32_t>(h, h->lay.meta);
   a.error_word = at<uint32_t>(h, h->lay.error_word);
+  if (d_extend_lens) {
+    if (!aligned(d_extend_lens, 4)) return PD_E_INVALID;
+    a.extend_lens = d_extend_lens;
+    a.qo_indptr = at<int32_t>(h, h->lay.qo_indptr);
+    a.item_indptr = at<int32_t>(h, h->lay.item_indptr);
+    a.group = h->cfg.n_heads / h->cfg.n_kv_heads;
+    a.n_kv_heads = h->cfg.n_kv_heads;
+  }
   return hip_status(pd::launch_bind(a, stream));
 }
 
@@ -271,6 +285,40 @@ pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, con
   a.k_layer = static_cast<uint16_t*>(d_k_store) + (int64_t)layer * layer_elems;
   a.v_layer = static_cast<uint16_t*>(d_v_store) + (int64_t)layer * layer_elems;
   return hip_status(pd::launch_append(a, stream));
+}
+
+pd_status paged_decode_bind_extend(pd_handle* h, int32_t batch, int32_t* d_seq_lens, const int32_t* d_extend_lens,
+                                   const int32_t* d_req_to_page, const int32_t* d_req_base, hipStream_t stream) {
+  if (!d_extend_lens || (d_req_to_page == nullptr) == (d_req_base == nullptr)) return PD_E_INVALID;
+  return pdh::bind_launch(h, batch, PD_BIND_FULL, d_seq_lens, nullptr, d_req_to_page, d_req_base, nullptr, stream,
+                          d_extend_lens);
+}
+
+pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q,
+                                    const void* d_k_store, const void* d_v_store, float scale, void* d_out,
+                                    hipStream_t stream) {
+  if (!h || !d_q || !d_k_store || !d_v_store || !d_out || batch < 1 || layer < 0) return PD_E_INVALID;
+  if (!aligned(d_q, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16) || !aligned(d_out, 16))
+    return PD_E_INVALID;
+  const pd_config& c = h->cfg;
+  if (batch > c.max_batch || layer >= c.n_layers) return PD_E_CAPACITY;
+  const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
+  pd::PrefillArgs a{};
+  a.batch = batch;
+  a.n_heads = c.n_heads;
+  a.n_kv_heads = c.n_kv_heads;
+  a.group = c.n_heads / c.n_kv_heads;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.q = static_cast<const uint16_t*>(d_q);
+  a.k_layer = static_cast<const uint16_t*>(d_k_store) + (int64_t)layer * layer_elems;
+  a.v_layer = static_cast<const uint16_t*>(d_v_store) + (int64_t)layer * layer_elems;
+  a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
+  a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
+  a.qo_indptr = at<int32_t>(h, h->lay.qo_indptr);
+  a.item_indptr = at<int32_t>(h, h->lay.item_indptr);
+  a.meta = at<int32_t>(h, h->lay.meta);
+  a.out = static_cast<uint16_t*>(d_out);
+  return hip_status(pd::launch_prefill(a, c.head_dim, stream));
 }
 
 pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,

@@ -26,7 +26,7 @@ int32_t auto_splits(const pd_handle* h, int32_t batch);
 
 pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens, int32_t* d_position_ids,
                       const int32_t* d_req_to_page, const int32_t* d_req_base, const int32_t* d_active,
-                      hipStream_t stream);
+                      hipStream_t stream, const int32_t* d_extend_lens = nullptr);
 
 pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
                       const void* d_k_new, const void* d_v_new, const void* d_k_store, const void* d_v_store,

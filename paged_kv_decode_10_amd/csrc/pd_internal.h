@@ -15,6 +15,8 @@ enum MetaWord : int {
   kMetaTotalTokens = 1,  // sum of the (clamped) lengths
   kMetaTotalPages = 2,   // sum over requests of ceil(L_b / page_size)
   kMetaActive = 4,       // active requests of a padded graph-pool step (graph pool only)
+  kMetaTotalQ = 5,       // extend bind: sum of the (clamped) new-token counts
+  kMetaTotalItems = 6,   // extend bind: prefill work items (request, kv head, 16 query rows)
 };
 
 // The attention launches this many waves.  They work in teams of
@@ -55,6 +57,14 @@ struct BindArgs {
   int32_t* page_indptr;       // [batch + 1]: prefix sum of ceil(L_b / page_size)
   int32_t* meta;
   uint32_t* error_word;
+  // extend bind only (else null): new tokens per request, and the prefix sums
+  // of the new-token counts and of the prefill work items per request
+  // (n_kv_heads * ceil(n_b * group / 16)).
+  const int32_t* extend_lens;
+  int32_t* qo_indptr;
+  int32_t* item_indptr;
+  int32_t group;
+  int32_t n_kv_heads;
 };
 
 struct AttnArgs {
@@ -109,7 +119,25 @@ struct AppendArgs {
   uint16_t* v_layer;
 };
 
+struct PrefillArgs {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t group;
+  float scale_log2;
+  const uint16_t* q;          // bf16 [total new tokens, n_heads, D], ragged by qo_indptr
+  const uint16_t* k_layer;
+  const uint16_t* v_layer;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* qo_indptr;
+  const int32_t* item_indptr;
+  const int32_t* meta;
+  uint16_t* out;              // bf16 [total new tokens, n_heads, D]
+};
+
 hipError_t launch_bind(const BindArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

@@ -1,0 +1,235 @@
+// Paged prefill / extend attention for gfx950 (CDNA4).
+//
+// AstrAI commits 0b661bae / cbc58447 (workspace.py and cache.py views): the
+// prefill qo_indptr is built once per step in the workspace and reused by
+// every layer's prefill, like kv_indptr for decode.  Here request b's last
+// n_b cached tokens are new, each with a query row (rows ragged by
+// qo_indptr); new token i sits at position p = L_b - n_b + i and attends
+// causally to the cached tokens 0 .. p of its request.
+//
+// Work item = (request b, kv head g, tile of 16 query rows).  The rows of a
+// request and kv head are its (new token i, query head hh) pairs, token major,
+// hh in [0, G): tile t holds rows 16t .. 16t+15, so a tile covers 16/G new
+// tokens (G <= 16).  The launch is persistent: wave w takes items w, w + 2048,
+// ... (item_indptr, built by the extend bind, gives each request's first
+// item).  Each item walks its request's tokens 0 .. p_max in 16-token units,
+// with the decode kernel's matrix-core scheme:
+//   scores  S[token][row] = K[16 x D] . Q^T[D x 16] on v_mfma_f32_16x16x32_bf16,
+//           the K rows loaded straight into the A-operand layout and the q of
+//           the 16 rows held as the B operand for the whole item;
+//   p       exp2 with a lazily raised reference max (rescale only when a score
+//           passes it by more than 8 in log2 units); tokens past a row's
+//           causal limit are -inf;
+//   p.V     v_mfma_f32_16x16x16_bf16 with p (bf16) as the A operand, exactly
+//           where the score MFMA left it, and the V rows packed pairwise.
+// The K/V tiles of unit u+1 and the slots of unit u+2 are in flight while
+// unit u is computed.  Outputs are normalised and rounded to bf16.
+#include "pd_internal.h"
+
+namespace pd {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kWavesTotal = 2048;
+constexpr float kSlack = 8.0f;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+template <int VE>
+struct VRow;
+template <>
+struct VRow<8> {
+  uint4 u;
+  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w; }
+};
+template <>
+struct VRow<4> {
+  uint2 u;
+  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : u.y; }
+};
+
+template <int D>
+struct KVTile {
+  static constexpr int KS = D / 32;
+  static constexpr int VE = D / 16;
+  uint4 k[KS];
+  VRow<VE> v[4];
+};
+
+// K rows of unit tokens (lane c: token c, chunks 16r + 64s) and V rows (lane
+// 16r + c: tokens 4r+i, chunk c), for the slot each lane c holds.
+template <int D>
+__device__ __forceinline__ KVTile<D> load_kv(const PrefillArgs& a, int32_t slot, int g, int r, int c) {
+  KVTile<D> t;
+  constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
+  const int64_t stride = (int64_t)a.n_kv_heads * D;
+  const uint16_t* kp = a.k_layer + (int64_t)slot * stride + (int64_t)g * D + 8 * r;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) t.k[s] = *reinterpret_cast<const uint4*>(kp + 32 * s);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t sv = __shfl(slot, 4 * r + i, 64);
+    const uint16_t* vp = a.v_layer + (int64_t)sv * stride + (int64_t)g * D + VE * c;
+    if constexpr (VE == 8) t.v[i].u = *reinterpret_cast<const uint4*>(vp);
+    else t.v[i].u = *reinterpret_cast<const uint2*>(vp);
+  }
+  return t;
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2)
+prefill_kernel(PrefillArgs a) {
+  constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int B = a.batch, G = a.group, H = a.n_heads, Hkv = a.n_kv_heads;
+  const int total_items = a.meta[kMetaTotalItems];
+
+  for (int item = w; item < total_items; item += kWavesTotal) {
+    // ---- locate the item: request b holds items [item_indptr[b], item_indptr[b+1]) ----
+    int cnt = 0;
+    for (int i0 = 0; i0 <= B; i0 += 64) {
+      const int i = i0 + lane;
+      const bool le = i <= B && a.item_indptr[i <= B ? i : B] <= item;
+      cnt += __popcll(__builtin_amdgcn_ballot_w64(le));
+    }
+    const int b = __builtin_amdgcn_readfirstlane(cnt - 1);
+    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[b]);
+    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[b + 1]);
+    const int tiles = (i_hi - i_lo) / Hkv;  // per kv head
+    const int k = item - i_lo;
+    const int g = k / tiles, tile = k % tiles;
+    const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
+    const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
+    const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
+    const int n = __builtin_amdgcn_readfirstlane(a.qo_indptr[b + 1]) - q0;
+    // Column c of this tile: row 16*tile + c = (new token ic, head hh).
+    const int row_c = 16 * tile + c;
+    const int ic = row_c / G, hh = row_c % G;
+    const bool valid = ic < n;
+    const int pos_c = L - n + ic;  // causal limit (columns past the tokens see everything; never written)
+    const int last_tok = min(n - 1, (16 * tile + 15) / G);
+    const int kv_end = L - n + last_tok + 1;  // tokens 0 .. kv_end-1 are read
+    const int nunits = (kv_end + 15) / 16;
+
+    // q of column c as the B operand (zeros for columns past the new tokens).
+    uint4 qv[KS];
+    {
+      const uint16_t* qp = a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);
+        if (!valid) v = make_uint4(0, 0, 0, 0);
+        qv[s] = v;
+      }
+    }
+    // Slot of token 16u + c (lanes past the range read the last token: finite
+    // data, masked below).
+    auto slot_of = [&](int u) {
+      int t = 16 * u + c;
+      t = t < kv_end ? t : kv_end - 1;
+      return a.kv_indices[kv0 + t];
+    };
+
+    f32x4_t acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mref = -INFINITY, lsum = 0.f;
+
+    auto compute = [&](const KVTile<D>& T, int u) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[s]),
+                                                     __builtin_bit_cast(bf16x8_t, qv[s]), sc, 0, 0, 0);
+      float t[4];
+      bool need = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * u + 4 * r + i;
+        t[i] = (tok <= pos_c && tok < kv_end) ? sc[i] * a.scale_log2 : -INFINITY;
+        need |= t[i] > mref + kSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float cm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float mnew = fmaxf(mref, cm);
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+        lsum *= alpha;
+        mref = mnew;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float ar = __shfl(alpha, 4 * r + jj, 64);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[e][jj] *= ar;
+        }
+      }
+      bf16x4_t pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = t[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[i] - mref);
+        lsum += p;
+        pb[i] = (__bf16)p;
+      }
+      const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x2_t bv;
+        bv[0] = __builtin_amdgcn_perm(T.v[1].dw(e >> 1), T.v[0].dw(e >> 1), sel);
+        bv[1] = __builtin_amdgcn_perm(T.v[3].dw(e >> 1), T.v[2].dw(e >> 1), sel);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv), acc[e], 0, 0, 0);
+      }
+    };
+
+    // ---- pipeline: tile of unit u+1 and slots of unit u+2 in flight ----
+    int32_t s_next = slot_of(nunits > 1 ? 1 : 0);
+    KVTile<D> cur = load_kv<D>(a, slot_of(0), g, r, c);
+    for (int u = 0; u < nunits; ++u) {
+      const int32_t s_after = slot_of(u + 2 < nunits ? u + 2 : nunits - 1);
+      const KVTile<D> nxt = load_kv<D>(a, s_next, g, r, c);
+      compute(cur, u);
+      cur = nxt;
+      s_next = s_after;
+    }
+
+    // ---- finalize: per column, sum over the four row groups, normalise, bf16 ----
+    float l = lsum + __shfl_xor(lsum, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int col = 4 * r + jj;  // accumulator row = column
+      const float lc = __shfl(l, col, 64);
+      const int rc = 16 * tile + col;
+      const int i_tok = rc / G, h_in = rc % G;
+      if (i_tok < n) {
+        const float inv = 1.0f / lc;
+        uint16_t* dst = a.out + ((int64_t)(q0 + i_tok) * H + (int64_t)g * G + h_in) * D + VE * c;
+        __bf16 ob[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) ob[e] = (__bf16)(acc[e][jj] * inv);
+        if constexpr (VE == 8) *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, ob);
+        else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, ob);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pd

@@ -54,9 +54,10 @@ def test_workspace_bytes_and_validation(abi):
     c = _cfg(abi)
     assert L.paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == abi.PD_OK
     rows = 4 * 32 * 8
-    # kv_indptr, kv_indices, page_indptr, o_part, ml_part, meta, error word, each 256-aligned
+    # kv_indptr, kv_indices, page_indptr, o_part, ml_part, qo_indptr, item_indptr, meta, error word, 256-aligned
     al = lambda x: -(-x // 256) * 256
-    want = al(5 * 4) + al(1000 * 4) + al(5 * 4) + al(rows * 128 * 4) + al(rows * 2 * 4) + al(64) + al(4)
+    want = (al(5 * 4) + al(1000 * 4) + al(5 * 4) + al(rows * 128 * 4) + al(rows * 2 * 4) + al(5 * 4) + al(5 * 4)
+            + al(64) + al(4))
     assert n.value == want
     for bad, code in [(dict(head_dim=96), abi.PD_E_UNSUPPORTED), (dict(n_heads=30), abi.PD_E_UNSUPPORTED),
                       (dict(n_heads=8 * 17), abi.PD_E_UNSUPPORTED), (dict(page_size=0), abi.PD_E_INVALID),
@@ -82,6 +83,8 @@ def test_host_side_rejections(abi):
     assert L.paged_decode_bind_contiguous(None, 1, 0, None, None, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_attn(None, 1, 0, 1, None, None, None, 1.0, None) == abi.PD_E_INVALID
     assert L.paged_decode_merge(None, 1, 1, None, None) == abi.PD_E_INVALID
+    assert L.paged_decode_bind_extend(None, 1, None, None, None, None, None) == abi.PD_E_INVALID
+    assert L.paged_decode_prefill_attn(None, 1, 0, None, None, None, 1.0, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_kv(None, 1, 0, None, None, None, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_attn(None, 1, 0, 1, None, None, None, None, None, 1.0, None) == abi.PD_E_INVALID
     assert L.paged_decode_graph_pool_create(None, None, 0, ctypes.byref(h)) == abi.PD_E_INVALID

@@ -1,0 +1,120 @@
+"""GPU: paged prefill / extend attention (causal over the request's cache,
+ragged query rows) through the C ABI, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from paged_kv_decode_10_amd import PD_BIND_FULL, PD_ERR_EXTEND_OVER_LEN
+from tests.gpu_harness import assert_close_out, make_ws, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+
+
+def _run(w, layer=0, contiguous=False):
+    dev = to_device(w)
+    ext = w.meta["extend_lens"].cuda()
+    ws = make_ws(w)
+    if contiguous:
+        ws.bind_extend(w.batch, dev.seq_lens, ext, req_base=w.meta["req_base"].cuda())
+    else:
+        ws.bind_extend(w.batch, dev.seq_lens, ext, req_to_page=dev.req_to_page)
+    out = torch.full(dev.q[layer].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws.prefill_attn(w.batch, layer, dev.q[layer], dev.k, dev.v, w.scale, out)
+    torch.cuda.synchronize()
+    return ws, out.float().cpu().numpy()
+
+
+def _oracle(w, layer=0):
+    L = w.seq_lens.numpy()
+    n = w.meta["extend_lens"].numpy()
+    if w.meta.get("layout") == "contiguous":
+        ix = oracle.kv_indices_contiguous(L, w.meta["req_base"].numpy())
+        ip = oracle.kv_indptr(L)
+    else:
+        ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    return oracle.prefill_attention(w.q[layer], w.k_store[layer], w.v_store[layer], L, n, ip, ix, w.scale,
+                                    w.n_kv_heads)
+
+
+def test_prefill_tiny():
+    say("[prefill] tiny")
+    w = workloads.make("prefill_tiny")
+    ws, got = _run(w)
+    assert ws.read_error() == 0
+    assert ws.qo_indptr[:3].cpu().tolist() == oracle.qo_indptr(w.meta["extend_lens"].numpy()).tolist()
+    ref, _ = _oracle(w)
+    assert np.isfinite(got).all()
+    assert_close_out(got, ref, "prefill tiny")
+
+
+@pytest.mark.parametrize("G,hkv,D,ps", [(1, 4, 128, 16), (2, 2, 64, 16), (4, 8, 128, 16), (8, 1, 128, 32),
+                                        (16, 2, 64, 16), (3, 2, 128, 7), (4, 2, 128, 1)])
+def test_prefill_shapes(G, hkv, D, ps):
+    say(f"[prefill] G={G} hkv={hkv} D={D} ps={ps}")
+    w = workloads.make_custom("pshape", seed=200 + G * 3 + D + ps, n_layers=2,
+                              seq_lens=[1, 37, 300, 64, 17, 90], extend_lens=[1, 37, 45, 1, 0, 33],
+                              n_heads=G * hkv, n_kv_heads=hkv, head_dim=D, page_size=ps)
+    ws, got = _run(w, layer=1)
+    assert ws.read_error() == 0
+    ref, _ = _oracle(w, layer=1)
+    assert_close_out(got, ref, "prefill shapes")
+
+
+def test_prefill_one_new_token_equals_decode():
+    """n_b = 1: each request's single query is the decode query over all L_b tokens."""
+    say("[prefill] n=1 vs decode")
+    w = workloads.make_custom("pdec", seed=210, n_layers=1, seq_lens=[100, 1, 2000, 513], extend_lens=[1, 1, 1, 1],
+                              n_heads=32, n_kv_heads=8, head_dim=128, page_size=16)
+    ws, got = _run(w)
+    L = w.seq_lens.numpy()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    ref, _ = oracle.decode_attention(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale, w.n_kv_heads)
+    assert_close_out(got, ref, "prefill n=1")
+
+
+def test_prefill_fresh_prompt_first_token_bit_exact():
+    """No prefix: token 0 of a fresh prompt sees only itself -> its V row exactly."""
+    w = workloads.make("prefill_tiny")
+    _, got = _run(w)
+    slot0 = int(w.req_to_page[0, 0]) * w.page_size
+    for h in range(w.n_heads):
+        assert np.array_equal(got[0, h], w.v_store[0, slot0, h // w.group].float().numpy()), h
+
+
+def test_prefill_contiguous_layout():
+    say("[prefill] contiguous")
+    w = workloads.make_custom("pcont", seed=220, n_layers=1, seq_lens=[500, 64, 1200], extend_lens=[200, 64, 7],
+                              n_heads=16, n_kv_heads=4, head_dim=128, page_size=16, layout="contiguous")
+    ws, got = _run(w, contiguous=True)
+    assert ws.read_error() == 0
+    ref, _ = _oracle(w)
+    assert_close_out(got, ref, "prefill contiguous")
+
+
+def test_prefill_config():
+    say("[prefill] 4 requests, extends of 64..1024 new tokens over prefixes")
+    w = workloads.make("prefill")
+    ws, got = _run(w)
+    assert ws.read_error() == 0
+    ref, _ = _oracle(w)
+    assert_close_out(got, ref, "prefill config")
+
+
+def test_extend_over_length_is_flagged():
+    w = workloads.make_custom("pbad", seed=230, n_layers=1, seq_lens=[20, 30], extend_lens=[5, 10], n_heads=4,
+                              n_kv_heads=2, head_dim=64, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w)
+    ext = torch.tensor([25, 10], dtype=torch.int32, device="cuda")
+    ws.bind_extend(w.batch, dev.seq_lens, ext, req_to_page=dev.req_to_page)
+    torch.cuda.synchronize()
+    assert ws.read_error() & PD_ERR_EXTEND_OVER_LEN
+    assert ws.qo_indptr[:3].cpu().tolist() == [0, 20, 30]
