@@ -255,6 +255,64 @@ def pool_sweep(batches, steps: int, warmup: int):
     return rows, keys
 
 
+def prefill_bench(name: str, reps: int):
+    """Prefill / extend attention on a prefill workload, one launch at a time
+    with the caches flushed: HIP-event median, algorithmic flops (QK^T and PV
+    over each query's causal range) and the K/V bytes the kernel streams
+    (every tile of 16 query rows reads its causal range once)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_decode_10_amd import Config, PagedDecode
+
+    w = workloads.make(name)
+    B, H, Hkv, D = w.batch, w.n_heads, w.n_kv_heads, w.head_dim
+    G = H // Hkv
+    cfg = Config(n_layers=w.n_layers, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size, max_batch=B,
+                 max_splits=8, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
+                 max_total_tokens=int(w.seq_lens.sum()))
+    ws = PagedDecode(cfg)
+    seq, tab = w.seq_lens.cuda(), w.req_to_page.cuda()
+    ext = w.meta["extend_lens"].cuda()
+    q, kst, vst = w.q.cuda(), w.k_store.cuda(), w.v_store.cuda()
+    out = torch.empty_like(q[0])
+    ws.bind_extend(B, seq, ext, req_to_page=tab)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for r in range(reps + 2):
+        flush.fill_(r)
+        e0.record()
+        ws.prefill_attn(B, 0, q[0], kst, vst, w.scale, out)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ts.append(e0.elapsed_time(e1) * 1e3)
+    assert ws.read_error() == 0 and torch.isfinite(out.float()).all()
+    L = w.seq_lens.numpy().astype(np.int64)
+    n = w.meta["extend_lens"].numpy().astype(np.int64)
+    keys = sum(int(((L[b] - n[b]) + np.arange(n[b]) + 1).sum()) for b in range(B))  # causal key count per query
+    flops = 4 * D * H * keys  # 2 flops per MAC, QK^T and PV
+    streamed = 0
+    for b in range(B):
+        for t in range(-(-int(n[b]) * G // 16)):
+            last = min(int(n[b]) - 1, (16 * t + 15) // G)
+            streamed += (int(L[b] - n[b]) + last + 1) * D * 2 * 2 * Hkv
+    kv_unique = int(L.sum()) * Hkv * D * 4
+    us = float(np.median(ts))
+    rec = {"workload": name, "batch": B, "new_tokens": int(n.sum()), "cached_tokens": int(L.sum()),
+           "us": round(us, 2), "p10_us": round(float(np.percentile(ts, 10)), 2),
+           "p90_us": round(float(np.percentile(ts, 90)), 2),
+           "tflops": round(flops / us / 1e6, 1), "mfma_bf16_peak_tflops": 2500.0,
+           "frac_of_mfma_peak": round(flops / us / 1e6 / 2500.0, 4),
+           "kv_bytes_streamed": streamed, "kv_streamed_gbs": round(streamed / us / 1e3, 1),
+           "kv_bytes_unique": kv_unique}
+    log(f"[prefill] {name}: {us:.1f} us, {rec['tflops']} TFLOP/s ({100 * rec['frac_of_mfma_peak']:.1f}% of bf16 "
+        f"MFMA), K/V streamed {streamed / 1e6:.0f} MB -> {rec['kv_streamed_gbs']} GB/s (unique {kv_unique / 1e6:.0f} MB)")
+    return rec
+
+
 def oracle_time(w, budget_s: float):
     """The oracle's decode attention on (request, kv head) pairs of the same
     inputs until about budget_s, scaled to KV bytes per second."""
@@ -292,6 +350,9 @@ def main() -> int:
                          "NAME@contiguous for the contiguous-cache layout) timed one launch at a time with the "
                          "caches flushed; prints one JSON line")
     ap.add_argument("--config-reps", type=int, default=20)
+    ap.add_argument("--prefill", default="",
+                    help="instead of the step: comma-separated prefill workloads (e.g. prefill) timed one launch at "
+                         "a time with the caches flushed; prints one JSON line")
     ap.add_argument("--pool", default="",
                     help="instead of the step: comma-separated batch sizes run through the graph pool (replayed "
                          "and eager) on the 24-layer step workload; prints one JSON line")
@@ -314,6 +375,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 2
+    if args.prefill:
+        rows = [prefill_bench(x, args.config_reps) for x in args.prefill.split(",") if x]
+        print(json.dumps({"metric": "paged prefill attention", "unit": "TFLOP/s", "n_gpus": 1, "data": "synthetic",
+                          "dtype": "bf16", "workloads": rows}), flush=True)
+        return 0
     if args.pool:
         rows, keys = pool_sweep([int(x) for x in args.pool.split(",") if x], args.steps, args.warmup)
         print(json.dumps({"metric": "graph pool: decode step time, replay vs eager", "unit": "us/step",
