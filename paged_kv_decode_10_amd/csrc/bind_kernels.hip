@@ -96,14 +96,14 @@ bind_scan_kernel(BindArgs a) {
   if (a.extend_lens != nullptr) {
     // Extend / prefill: the last n_b of the (clipped) tokens are new, one
     // query row each; qo_indptr is the prefix sum of n_b, and item_indptr that
-    // of the work items n_kv_heads * ceil(n_b * group / 16).
+    // of the work items n_kv_heads * ceil(n_b * group / kPrefillRows).
     int64_t nb = 0;
     if (b < B) {
       nb = a.extend_lens[b];
       if (nb < 0) { nb = 0; flags |= PD_ERR_NEG_SEQ_LEN; }
       if (nb > hi - lo) { nb = hi - lo; flags |= PD_ERR_EXTEND_OVER_LEN; }
     }
-    const int64_t items = (int64_t)a.n_kv_heads * ((nb * a.group + 15) / 16);
+    const int64_t items = (int64_t)a.n_kv_heads * ((nb * a.group + kPrefillRows - 1) / kPrefillRows);
     const int64_t qincl = wave_inclusive_scan(nb);
     const int64_t iincl = wave_inclusive_scan(items);
     __syncthreads();  // wave_tot is reused

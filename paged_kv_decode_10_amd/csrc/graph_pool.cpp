@@ -65,7 +65,7 @@ pd_status launch_step(pd_graph_pool* p, int i, hipStream_t stream) {
 
 void release_graphs(pd_graph_pool* p) {
   for (int i = 0; i < p->n_keys; ++i) {
-    if (p->exec[i]) hipGraphExecDestroy(p->exec[i]);
+    if (p->exec[i]) (void)hipGraphExecDestroy(p->exec[i]);
     p->exec[i] = nullptr;
   }
 }
@@ -122,7 +122,7 @@ pd_status paged_decode_graph_pool_warmup(pd_graph_pool* p) {
       hipGraphExec_t ex = nullptr;
       if (hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) == hipSuccess) p->exec[i] = ex;
     }
-    if (g) hipGraphDestroy(g);
+    if (g) (void)hipGraphDestroy(g);
     (void)hipGetLastError();  // a failed key runs eagerly; clear its error
   }
   return PD_OK;
@@ -157,7 +157,7 @@ pd_status paged_decode_graph_pool_key(const pd_graph_pool* p, int32_t index, int
 pd_status paged_decode_graph_pool_destroy(pd_graph_pool* p) {
   if (!p) return PD_E_INVALID;
   release_graphs(p);
-  if (p->capture_stream) hipStreamDestroy(p->capture_stream);
+  if (p->capture_stream) (void)hipStreamDestroy(p->capture_stream);
   delete p;
   return PD_OK;
 }

@@ -16,7 +16,7 @@ enum MetaWord : int {
   kMetaTotalPages = 2,   // sum over requests of ceil(L_b / page_size)
   kMetaActive = 4,       // active requests of a padded graph-pool step (graph pool only)
   kMetaTotalQ = 5,       // extend bind: sum of the (clamped) new-token counts
-  kMetaTotalItems = 6,   // extend bind: prefill work items (request, kv head, 16 query rows)
+  kMetaTotalItems = 6,   // extend bind: prefill work items (request, kv head, query rows)
 };
 
 // The attention launches this many waves.  They work in teams of
@@ -59,7 +59,7 @@ struct BindArgs {
   uint32_t* error_word;
   // extend bind only (else null): new tokens per request, and the prefix sums
   // of the new-token counts and of the prefill work items per request
-  // (n_kv_heads * ceil(n_b * group / 16)).
+  // (n_kv_heads * ceil(n_b * group / kPrefillRows)).
   const int32_t* extend_lens;
   int32_t* qo_indptr;
   int32_t* item_indptr;
@@ -118,6 +118,14 @@ struct AppendArgs {
   uint16_t* k_layer;          // bf16 [num_slots, n_kv_heads, D] of this layer
   uint16_t* v_layer;
 };
+
+// Prefill work item: one request, one kv head, kPrefillRows query rows
+// (kPrefillTiles MFMA tiles of 16 (new token, query head) rows).
+#ifndef PD_PREFILL_TILES
+#define PD_PREFILL_TILES 2
+#endif
+constexpr int kPrefillTiles = PD_PREFILL_TILES;
+constexpr int kPrefillRows = 16 * kPrefillTiles;
 
 struct PrefillArgs {
   int32_t batch;

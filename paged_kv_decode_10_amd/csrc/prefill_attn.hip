@@ -7,12 +7,13 @@
 // qo_indptr); new token i sits at position p = L_b - n_b + i and attends
 // causally to the cached tokens 0 .. p of its request.
 //
-// Work item = (request b, kv head g, tile of 16 query rows).  The rows of a
-// request and kv head are its (new token i, query head hh) pairs, token major,
-// hh in [0, G): tile t holds rows 16t .. 16t+15, so a tile covers 16/G new
-// tokens (G <= 16).  The launch is persistent: wave w takes items w, w + 2048,
-// ... (item_indptr, built by the extend bind, gives each request's first
-// item).  Each item walks its request's tokens 0 .. p_max in 16-token units,
+// Work item = (request b, kv head g, kPrefillRows query rows, in tiles of 16).
+// The rows of a request and kv head are its (new token i, query head hh)
+// pairs, token major, hh in [0, G): item k holds rows kPrefillRows*k .. on, so
+// each 16-row MFMA tile covers 16/G new tokens (G <= 16).  The K and V tiles
+// of a unit are loaded once for all the item's query tiles.  The launch is
+// persistent: wave w takes items w, w + 2048, ... (item_indptr, built by the
+// extend bind, gives each request's first item).  Each item walks its request's tokens 0 .. p_max in 16-token units,
 // with the decode kernel's matrix-core scheme:
 //   scores  S[token][row] = K[16 x D] . Q^T[D x 16] on v_mfma_f32_16x16x32_bf16,
 //           the K rows loaded straight into the A-operand layout and the q of
@@ -81,10 +82,15 @@ __device__ __forceinline__ KVTile<D> load_kv(const PrefillArgs& a, int32_t slot,
   return t;
 }
 
+#ifndef PD_PREFILL_WAVES_PER_SIMD
+#define PD_PREFILL_WAVES_PER_SIMD 2
+#endif
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, PD_PREFILL_WAVES_PER_SIMD)
 prefill_kernel(PrefillArgs a) {
   constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
+  constexpr int NQ = kPrefillTiles;
   const int lane = threadIdx.x & 63;
   const int r = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
@@ -102,31 +108,35 @@ prefill_kernel(PrefillArgs a) {
     const int b = __builtin_amdgcn_readfirstlane(cnt - 1);
     const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[b]);
     const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[b + 1]);
-    const int tiles = (i_hi - i_lo) / Hkv;  // per kv head
+    const int groups = (i_hi - i_lo) / Hkv;  // items per kv head
     const int k = item - i_lo;
-    const int g = k / tiles, tile = k % tiles;
+    const int g = k / groups, grp = k % groups;
     const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
     const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
     const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
     const int n = __builtin_amdgcn_readfirstlane(a.qo_indptr[b + 1]) - q0;
-    // Column c of this tile: row 16*tile + c = (new token ic, head hh).
-    const int row_c = 16 * tile + c;
-    const int ic = row_c / G, hh = row_c % G;
-    const bool valid = ic < n;
-    const int pos_c = L - n + ic;  // causal limit (columns past the tokens see everything; never written)
-    const int last_tok = min(n - 1, (16 * tile + 15) / G);
+    // Tile x of the item holds rows kPrefillRows*grp + 16x + column; a row is
+    // (new token i, query head hh), token major.
+    const int row0 = kPrefillRows * grp;
+    const int last_tok = min(n - 1, (row0 + kPrefillRows - 1) / G);
     const int kv_end = L - n + last_tok + 1;  // tokens 0 .. kv_end-1 are read
     const int nunits = (kv_end + 15) / 16;
 
-    // q of column c as the B operand (zeros for columns past the new tokens).
-    uint4 qv[KS];
-    {
-      const uint16_t* qp = a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
+    uint4 qv[NQ][KS];
+    int pos_c[NQ];
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      const int rc = row0 + 16 * x + c;
+      const int ic = rc / G, hh = rc % G;
+      const bool valid = ic < n;
+      pos_c[x] = L - n + ic;  // causal limit of column c (rows past the tokens: never written)
+      const uint16_t* qp =
+          a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);
         if (!valid) v = make_uint4(0, 0, 0, 0);
-        qv[s] = v;
+        qv[x][s] = v;
       }
     }
     // Slot of token 16u + c (lanes past the range read the last token: finite
@@ -137,55 +147,67 @@ prefill_kernel(PrefillArgs a) {
       return a.kv_indices[kv0 + t];
     };
 
-    f32x4_t acc[VE];
+    f32x4_t acc[NQ][VE];
+    float mref[NQ], lsum[NQ];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mref = -INFINITY, lsum = 0.f;
+    for (int x = 0; x < NQ; ++x) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[x][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      mref[x] = -INFINITY;
+      lsum[x] = 0.f;
+    }
 
     auto compute = [&](const KVTile<D>& T, int u) {
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[s]),
-                                                     __builtin_bit_cast(bf16x8_t, qv[s]), sc, 0, 0, 0);
-      float t[4];
-      bool need = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * u + 4 * r + i;
-        t[i] = (tok <= pos_c && tok < kv_end) ? sc[i] * a.scale_log2 : -INFINITY;
-        need |= t[i] > mref + kSlack;
-      }
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        float cm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-        const float mnew = fmaxf(mref, cm);
-        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-        lsum *= alpha;
-        mref = mnew;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float ar = __shfl(alpha, 4 * r + jj, 64);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[e][jj] *= ar;
-        }
-      }
-      bf16x4_t pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = t[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[i] - mref);
-        lsum += p;
-        pb[i] = (__bf16)p;
-      }
-      const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
+      // V operand (shared by the tiles): element e of the four V rows, pairwise
+      u32x2_t bv[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2_t bv;
-        bv[0] = __builtin_amdgcn_perm(T.v[1].dw(e >> 1), T.v[0].dw(e >> 1), sel);
-        bv[1] = __builtin_amdgcn_perm(T.v[3].dw(e >> 1), T.v[2].dw(e >> 1), sel);
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv), acc[e], 0, 0, 0);
+        bv[e][0] = __builtin_amdgcn_perm(T.v[1].dw(e >> 1), T.v[0].dw(e >> 1), sel);
+        bv[e][1] = __builtin_amdgcn_perm(T.v[3].dw(e >> 1), T.v[2].dw(e >> 1), sel);
+      }
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) {
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[s]),
+                                                       __builtin_bit_cast(bf16x8_t, qv[x][s]), sc, 0, 0, 0);
+        float t[4];
+        bool need = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * u + 4 * r + i;
+          t[i] = (tok <= pos_c[x] && tok < kv_end) ? sc[i] * a.scale_log2 : -INFINITY;
+          need |= t[i] > mref[x] + kSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          float cm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+          cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+          cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+          const float mnew = fmaxf(mref[x], cm);
+          const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[x] - mnew);
+          lsum[x] *= alpha;
+          mref[x] = mnew;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float ar = __shfl(alpha, 4 * r + jj, 64);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[x][e][jj] *= ar;
+          }
+        }
+        bf16x4_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = t[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[i] - mref[x]);
+          lsum[x] += p;
+          pb[i] = (__bf16)p;
+        }
+        const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          acc[x][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv[e]), acc[x][e],
+                                                                 0, 0, 0);
       }
     };
 
@@ -201,22 +223,25 @@ prefill_kernel(PrefillArgs a) {
     }
 
     // ---- finalize: per column, sum over the four row groups, normalise, bf16 ----
-    float l = lsum + __shfl_xor(lsum, 16, 64);
-    l += __shfl_xor(l, 32, 64);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int col = 4 * r + jj;  // accumulator row = column
-      const float lc = __shfl(l, col, 64);
-      const int rc = 16 * tile + col;
-      const int i_tok = rc / G, h_in = rc % G;
-      if (i_tok < n) {
-        const float inv = 1.0f / lc;
-        uint16_t* dst = a.out + ((int64_t)(q0 + i_tok) * H + (int64_t)g * G + h_in) * D + VE * c;
-        __bf16 ob[VE];
+    for (int x = 0; x < NQ; ++x) {
+      float l = lsum[x] + __shfl_xor(lsum[x], 16, 64);
+      l += __shfl_xor(l, 32, 64);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) ob[e] = (__bf16)(acc[e][jj] * inv);
-        if constexpr (VE == 8) *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, ob);
-        else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, ob);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = 4 * r + jj;  // accumulator row = column
+        const float lc = __shfl(l, col, 64);
+        const int rc = row0 + 16 * x + col;
+        const int i_tok = rc / G, h_in = rc % G;
+        if (i_tok < n) {
+          const float inv = 1.0f / lc;
+          uint16_t* dst = a.out + ((int64_t)(q0 + i_tok) * H + (int64_t)g * G + h_in) * D + VE * c;
+          __bf16 ob[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) ob[e] = (__bf16)(acc[x][e][jj] * inv);
+          if constexpr (VE == 8) *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, ob);
+          else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, ob);
+        }
       }
     }
   }
