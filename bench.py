@@ -126,7 +126,7 @@ def cpu_baseline(w, budget_s: float, num_splits: int):
                       f"BLAS threads {blas}; numpy {np.__version__}"}
 
 
-def config_sweep(names, reps: int, oracle_budget: float):
+def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0):
     """Per-config attention and merge timings with the caches flushed.
 
     For each workload: one bind, then ``reps`` iterations of [1 GiB
@@ -157,7 +157,7 @@ def config_sweep(names, reps: int, oracle_budget: float):
         seq, pos, tab = w.seq_lens.cuda(), w.position_ids.cuda(), w.req_to_page.cuda()
         q, kst, vst = w.q.cuda(), w.k_store.cuda(), w.v_store.cuda()
         out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
-        S = ws.num_splits(B)
+        S = ws.num_splits(B, splits)
         if layout == "contiguous":
             ws.bind_contiguous(B, PD_BIND_FULL, seq, pos, w.meta["req_base"].cuda())
         else:
@@ -388,7 +388,8 @@ def main() -> int:
               flush=True)
         return 0
     if args.configs:
-        rows = config_sweep([x for x in args.configs.split(",") if x], args.config_reps, args.oracle_budget)
+        rows = config_sweep([x for x in args.configs.split(",") if x], args.config_reps, args.oracle_budget,
+                            args.splits)
         print(json.dumps({"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "data": "synthetic", "dtype": "bf16",
                           "timing": "HIP events per launch, 1 GiB flush-write before each iteration",
                           "configs": rows}), flush=True)
