@@ -227,11 +227,13 @@ pd_status paged_decode_bind_extend(pd_handle* h, int32_t batch, int32_t* d_seq_l
  * p = L_b - n_b + i) attends to that request's tokens 0 .. p:
  *   out[row, h, :] = sum_t softmax_t(scale * q[row, h] . K_t) V_t   (t <= p),
  * kv head of query head h = h / (n_heads / n_kv_heads); rounded to bf16.
- *   d_q    bf16 [sum n_b, n_heads, head_dim] (rows ragged by qo_indptr)
- *   d_out  bf16 [sum n_b, n_heads, head_dim], caller-owned
+ *   d_q     bf16 [q_rows, n_heads, head_dim] (rows ragged by qo_indptr)
+ *   q_rows  rows the caller allocated in d_q and d_out: query rows at or past
+ *           it (sum n_b > q_rows) are not computed and set PD_ERR_TOTAL_OVER_CAP
+ *   d_out   bf16 [q_rows, n_heads, head_dim], caller-owned
  *   stores as in paged_decode_attn.  Reads the last extend bind.  One
- * persistent launch (2048 waves over (request, kv head, 16 query rows)). */
-pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q,
+ * persistent launch (2048 waves over (request, kv head, 32 query rows)). */
+pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q, int32_t q_rows,
                                     const void* d_k_store, const void* d_v_store, float scale, void* d_out,
                                     hipStream_t stream);
 

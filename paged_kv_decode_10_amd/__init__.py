@@ -234,8 +234,8 @@ class PagedDecode:
         p_k = _dev_ptr(k_store, torch.bfloat16, "k_store", store_numel)
         p_v = _dev_ptr(v_store, torch.bfloat16, "v_store", store_numel)
         _abi.check("paged_decode_prefill_attn",
-                   _abi.lib().paged_decode_prefill_attn(self._h, batch, layer, p_q, p_k, p_v, float(scale), p_o,
-                                                        _stream_ptr(stream)))
+                   _abi.lib().paged_decode_prefill_attn(self._h, batch, layer, p_q, int(q.shape[0]), p_k, p_v,
+                                                        float(scale), p_o, _stream_ptr(stream)))
 
     @property
     def qo_indptr(self):

@@ -118,7 +118,7 @@ def lib() -> ctypes.CDLL:
         "paged_decode_append_attn": [P, I32, I32, I32, P, P, P, P, P, F, P],
         "paged_decode_merge": [P, I32, I32, P, P],
         "paged_decode_bind_extend": [P, I32, P, P, P, P, P],
-        "paged_decode_prefill_attn": [P, I32, I32, P, P, P, F, P, P],
+        "paged_decode_prefill_attn": [P, I32, I32, P, I32, P, P, F, P, P],
         "paged_decode_graph_pool_create": [P, ctypes.POINTER(PdStepBuffers), ctypes.c_uint32, ctypes.POINTER(P)],
         "paged_decode_graph_pool_warmup": [P],
         "paged_decode_graph_pool_step": [P, I32, P],

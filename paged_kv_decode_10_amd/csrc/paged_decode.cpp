@@ -294,10 +294,11 @@ pd_status paged_decode_bind_extend(pd_handle* h, int32_t batch, int32_t* d_seq_l
                           d_extend_lens);
 }
 
-pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q,
+pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q, int32_t q_rows,
                                     const void* d_k_store, const void* d_v_store, float scale, void* d_out,
                                     hipStream_t stream) {
-  if (!h || !d_q || !d_k_store || !d_v_store || !d_out || batch < 1 || layer < 0) return PD_E_INVALID;
+  if (!h || !d_q || !d_k_store || !d_v_store || !d_out || batch < 1 || layer < 0 || q_rows < 0)
+    return PD_E_INVALID;
   if (!aligned(d_q, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16) || !aligned(d_out, 16))
     return PD_E_INVALID;
   const pd_config& c = h->cfg;
@@ -310,11 +311,13 @@ pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, 
   a.group = c.n_heads / c.n_kv_heads;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   a.q = static_cast<const uint16_t*>(d_q);
+  a.q_rows = q_rows;
   a.k_layer = static_cast<const uint16_t*>(d_k_store) + (int64_t)layer * layer_elems;
   a.v_layer = static_cast<const uint16_t*>(d_v_store) + (int64_t)layer * layer_elems;
   a.kv_indptr = at<int32_t>(h, h->lay.kv_indptr);
   a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
   a.qo_indptr = at<int32_t>(h, h->lay.qo_indptr);
+  a.error_word = at<uint32_t>(h, h->lay.error_word);
   a.item_indptr = at<int32_t>(h, h->lay.item_indptr);
   a.meta = at<int32_t>(h, h->lay.meta);
   a.out = static_cast<uint16_t*>(d_out);

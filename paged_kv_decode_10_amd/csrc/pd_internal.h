@@ -133,7 +133,8 @@ struct PrefillArgs {
   int32_t n_kv_heads;
   int32_t group;
   float scale_log2;
-  const uint16_t* q;          // bf16 [total new tokens, n_heads, D], ragged by qo_indptr
+  const uint16_t* q;          // bf16 [q_rows, n_heads, D], ragged by qo_indptr
+  int32_t q_rows;             // rows of q and out: rows at or past it are not computed
   const uint16_t* k_layer;
   const uint16_t* v_layer;
   const int32_t* kv_indptr;
@@ -141,7 +142,8 @@ struct PrefillArgs {
   const int32_t* qo_indptr;
   const int32_t* item_indptr;
   const int32_t* meta;
-  uint16_t* out;              // bf16 [total new tokens, n_heads, D]
+  uint16_t* out;              // bf16 [q_rows, n_heads, D]
+  uint32_t* error_word;
 };
 
 hipError_t launch_bind(const BindArgs& a, hipStream_t stream);

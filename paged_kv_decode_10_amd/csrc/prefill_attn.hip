@@ -114,12 +114,17 @@ prefill_kernel(PrefillArgs a) {
     const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
     const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
     const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
-    const int n = __builtin_amdgcn_readfirstlane(a.qo_indptr[b + 1]) - q0;
+    const int n_all = __builtin_amdgcn_readfirstlane(a.qo_indptr[b + 1]) - q0;
+    // Query rows past the caller's q / out capacity are not computed (flagged).
+    const int n = min(n_all, max(a.q_rows - q0, 0));
+    if (n < n_all && lane == 0) atomicOr(a.error_word, PD_ERR_TOTAL_OVER_CAP);
+    if (n <= 0) continue;
     // Tile x of the item holds rows kPrefillRows*grp + 16x + column; a row is
     // (new token i, query head hh), token major.
     const int row0 = kPrefillRows * grp;
+    if (row0 >= n * G) continue;  // every row of the item is past the capacity
     const int last_tok = min(n - 1, (row0 + kPrefillRows - 1) / G);
-    const int kv_end = L - n + last_tok + 1;  // tokens 0 .. kv_end-1 are read
+    const int kv_end = L - n_all + last_tok + 1;  // tokens 0 .. kv_end-1 are read
     const int nunits = (kv_end + 15) / 16;
 
     uint4 qv[NQ][KS];
@@ -129,7 +134,7 @@ prefill_kernel(PrefillArgs a) {
       const int rc = row0 + 16 * x + c;
       const int ic = rc / G, hh = rc % G;
       const bool valid = ic < n;
-      pos_c[x] = L - n + ic;  // causal limit of column c (rows past the tokens: never written)
+      pos_c[x] = L - n_all + ic;  // causal limit of column c (rows past the tokens: never written)
       const uint16_t* qp =
           a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
 #pragma unroll

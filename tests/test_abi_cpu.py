@@ -84,7 +84,7 @@ def test_host_side_rejections(abi):
     assert L.paged_decode_attn(None, 1, 0, 1, None, None, None, 1.0, None) == abi.PD_E_INVALID
     assert L.paged_decode_merge(None, 1, 1, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_bind_extend(None, 1, None, None, None, None, None) == abi.PD_E_INVALID
-    assert L.paged_decode_prefill_attn(None, 1, 0, None, None, None, 1.0, None, None) == abi.PD_E_INVALID
+    assert L.paged_decode_prefill_attn(None, 1, 0, None, 0, None, None, 1.0, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_kv(None, 1, 0, None, None, None, None, None) == abi.PD_E_INVALID
     assert L.paged_decode_append_attn(None, 1, 0, 1, None, None, None, None, None, 1.0, None) == abi.PD_E_INVALID
     assert L.paged_decode_graph_pool_create(None, None, 0, ctypes.byref(h)) == abi.PD_E_INVALID

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from paged_kv_decode_10_amd import PD_BIND_FULL, PD_ERR_EXTEND_OVER_LEN
+from paged_kv_decode_10_amd import PD_ERR_EXTEND_OVER_LEN, PD_ERR_TOTAL_OVER_CAP
 from tests.gpu_harness import assert_close_out, make_ws, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -106,6 +106,24 @@ def test_prefill_config():
     assert ws.read_error() == 0
     ref, _ = _oracle(w)
     assert_close_out(got, ref, "prefill config")
+
+
+def test_rows_past_the_q_capacity_are_not_computed():
+    """q / out hold fewer rows than the extend bind's total: the rows past them
+    are skipped (nothing is read or written out of bounds) and flagged."""
+    w = workloads.make("prefill_tiny")
+    dev = to_device(w)
+    ws = make_ws(w)
+    ws.bind_extend(w.batch, dev.seq_lens, w.meta["extend_lens"].cuda(), req_to_page=dev.req_to_page)
+    rows = 30  # of 52
+    q = dev.q[0][:rows].contiguous()
+    out = torch.full((rows + 8, w.n_heads, w.head_dim), 3.0, dtype=torch.bfloat16, device="cuda")
+    ws.prefill_attn(w.batch, 0, q, dev.k, dev.v, w.scale, out[:rows])
+    torch.cuda.synchronize()
+    assert ws.read_error() & PD_ERR_TOTAL_OVER_CAP
+    ref, _ = _oracle(w)
+    assert_close_out(out[:rows].float().cpu().numpy(), ref[:rows], "prefill rows within the capacity")
+    assert torch.all(out[rows:].float() == 3.0)
 
 
 def test_extend_over_length_is_flagged():
