@@ -119,13 +119,19 @@ struct AppendArgs {
   uint16_t* v_layer;
 };
 
-// Prefill work item: one request, one kv head, kPrefillRows query rows
-// (kPrefillTiles MFMA tiles of 16 (new token, query head) rows).
+// Prefill work item: one request, one kv head, kPrefillRows query rows.  A
+// wave holds kPrefillTiles MFMA tiles of 16 (new token, query head) rows; with
+// PD_PREFILL_LDS the four waves of a workgroup share one item (and its K/V
+// tiles, staged in LDS), else each wave has an item of its own.
 #ifndef PD_PREFILL_TILES
 #define PD_PREFILL_TILES 2
 #endif
+#ifndef PD_PREFILL_LDS
+#define PD_PREFILL_LDS 1
+#endif
 constexpr int kPrefillTiles = PD_PREFILL_TILES;
-constexpr int kPrefillRows = 16 * kPrefillTiles;
+constexpr int kPrefillWavesPerItem = PD_PREFILL_LDS ? 4 : 1;
+constexpr int kPrefillRows = 16 * kPrefillTiles * kPrefillWavesPerItem;
 
 struct PrefillArgs {
   int32_t batch;

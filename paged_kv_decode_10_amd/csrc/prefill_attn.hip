@@ -252,13 +252,259 @@ prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Workgroup-cooperative variant: the four waves of a workgroup take the
+// item's consecutive 16*kPrefillTiles-row slices and share its K/V, which the
+// whole workgroup stages into LDS 64 tokens at a time (double buffered: stage
+// s+1 is fetched into registers while the four 16-token units of stage s are
+// computed from LDS, and the slots of stage s+2 are in flight).  Each K/V row
+// is read from memory once per item instead of once per wave, and one memory
+// round trip covers four units of compute.
+constexpr int kStageTok = 64;
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, PD_PREFILL_WAVES_PER_SIMD)
+prefill_lds_kernel(PrefillArgs a) {
+  constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
+  constexpr int NQ = kPrefillTiles;
+  constexpr int CPR = D / 8;                          // 16-byte chunks per K or V row
+  constexpr int RS = CPR + 1;                         // padded LDS row stride (uint4)
+  constexpr int kStageChunks = kStageTok * CPR;       // per tensor
+  constexpr int kPer = 2 * kStageChunks / kThreads;   // chunks a thread moves per stage (K then V)
+  __shared__ uint4 sK[2][kStageTok * RS];
+  __shared__ uint4 sV[2][kStageTok * RS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int B = a.batch, G = a.group, H = a.n_heads, Hkv = a.n_kv_heads;
+  const int total_items = a.meta[kMetaTotalItems];
+  const int64_t kv_stride = (int64_t)Hkv * D;
+
+  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+    int cnt = 0;
+    for (int i0 = 0; i0 <= B; i0 += 64) {
+      const int i = i0 + lane;
+      const bool le = i <= B && a.item_indptr[i <= B ? i : B] <= item;
+      cnt += __popcll(__builtin_amdgcn_ballot_w64(le));
+    }
+    const int b = __builtin_amdgcn_readfirstlane(cnt - 1);
+    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[b]);
+    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[b + 1]);
+    const int groups = (i_hi - i_lo) / Hkv;
+    const int k = item - i_lo;
+    const int g = k / groups, grp = k % groups;
+    const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
+    const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
+    const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
+    const int n_all = __builtin_amdgcn_readfirstlane(a.qo_indptr[b + 1]) - q0;
+    const int n = min(n_all, max(a.q_rows - q0, 0));
+    if (n < n_all && tid == 0) atomicOr(a.error_word, PD_ERR_TOTAL_OVER_CAP);
+    const int row0_item = kPrefillRows * grp;
+    if (n <= 0 || row0_item >= n * G) continue;  // the whole workgroup skips the item
+    // the item's K/V range (all four waves walk it; rows past their own
+    // causal limit are masked)
+    const int last_item_tok = min(n - 1, (row0_item + kPrefillRows - 1) / G);
+    const int kv_end = L - n_all + last_item_tok + 1;
+    const int nstages = (kv_end + kStageTok - 1) / kStageTok;
+    const int row0 = row0_item + 16 * NQ * wv;  // this wave's rows
+
+    uint4 qv[NQ][KS];
+    int pos_c[NQ];
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      const int rc = row0 + 16 * x + c;
+      const int ic = rc / G, hh = rc % G;
+      const bool valid = ic < n;
+      pos_c[x] = L - n_all + ic;
+      const uint16_t* qp =
+          a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);
+        if (!valid) v = make_uint4(0, 0, 0, 0);
+        qv[x][s] = v;
+      }
+    }
+    // Chunk m of this thread in a stage: index tid + kThreads*m over [K chunks | V chunks];
+    // its token is (index mod kStageChunks) / CPR.
+    auto chunk_tok = [&](int m) { return ((tid + kThreads * m) % kStageChunks) / CPR; };
+    auto slots_of = [&](int st, int32_t (&sl)[kPer]) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        int t = kStageTok * st + chunk_tok(m);
+        t = t < kv_end ? t : kv_end - 1;
+        sl[m] = a.kv_indices[kv0 + t];
+      }
+    };
+    auto fetch = [&](const int32_t (&sl)[kPer], uint4 (&v)[kPer]) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int idx = tid + kThreads * m;
+        const uint16_t* src = (idx < kStageChunks ? a.k_layer : a.v_layer);
+        const int ch = (idx % kStageChunks) % CPR;
+        v[m] = *reinterpret_cast<const uint4*>(src + (int64_t)sl[m] * kv_stride + (int64_t)g * D + 8 * ch);
+      }
+    };
+    auto stage_to_lds = [&](int buf, const uint4 (&v)[kPer]) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int idx = tid + kThreads * m;
+        const int loc = idx % kStageChunks;
+        uint4* dst = idx < kStageChunks ? sK[buf] : sV[buf];
+        dst[(loc / CPR) * RS + loc % CPR] = v[m];
+      }
+    };
+
+    f32x4_t acc[NQ][VE];
+    float mref[NQ], lsum[NQ];
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[x][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      mref[x] = -INFINITY;
+      lsum[x] = 0.f;
+    }
+
+    // 16-token unit `u` (absolute) whose rows start at row t0 of LDS buffer `buf`
+    auto compute = [&](int buf, int t0, int u) {
+      uint4 kk[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kk[s] = sK[buf][(t0 + c) * RS + r + 4 * s];  // token c, bytes 16r + 64s
+      u32x2_t bv[VE];
+      if constexpr (VE == 8) {
+        uint4 vr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[i] = sV[buf][(t0 + 4 * r + i) * RS + c];  // token 4r+i, chunk c
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const int dw = e >> 1;
+          auto pick = [&](const uint4& x) { return dw == 0 ? x.x : dw == 1 ? x.y : dw == 2 ? x.z : x.w; };
+          bv[e][0] = __builtin_amdgcn_perm(pick(vr[1]), pick(vr[0]), sel);
+          bv[e][1] = __builtin_amdgcn_perm(pick(vr[3]), pick(vr[2]), sel);
+        }
+      } else {
+        uint2 vr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // token 4r+i, 8 bytes at 8c
+          vr[i] = reinterpret_cast<const uint2*>(&sV[buf][(t0 + 4 * r + i) * RS])[c];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const int dw = e >> 1;
+          auto pick = [&](const uint2& x) { return dw == 0 ? x.x : x.y; };
+          bv[e][0] = __builtin_amdgcn_perm(pick(vr[1]), pick(vr[0]), sel);
+          bv[e][1] = __builtin_amdgcn_perm(pick(vr[3]), pick(vr[2]), sel);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) {
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                       __builtin_bit_cast(bf16x8_t, qv[x][s]), sc, 0, 0, 0);
+        float t[4];
+        bool need = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * u + 4 * r + i;
+          t[i] = (tok <= pos_c[x] && tok < kv_end) ? sc[i] * a.scale_log2 : -INFINITY;
+          need |= t[i] > mref[x] + kSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          float cm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+          cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+          cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+          const float mnew = fmaxf(mref[x], cm);
+          const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[x] - mnew);
+          lsum[x] *= alpha;
+          mref[x] = mnew;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float ar = __shfl(alpha, 4 * r + jj, 64);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[x][e][jj] *= ar;
+          }
+        }
+        bf16x4_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = t[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[i] - mref[x]);
+          lsum[x] += p;
+          pb[i] = (__bf16)p;
+        }
+        const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          acc[x][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv[e]), acc[x][e],
+                                                                 0, 0, 0);
+      }
+    };
+
+    // ---- pipeline over 64-token stages ----
+    __syncthreads();  // the previous item's last compute is done with the buffers
+    int32_t sl_next[kPer];
+    {
+      int32_t sl0[kPer];
+      uint4 v0[kPer];
+      slots_of(0, sl0);
+      fetch(sl0, v0);
+      stage_to_lds(0, v0);
+      slots_of(nstages > 1 ? 1 : 0, sl_next);
+    }
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+      int32_t sl_after[kPer];
+      slots_of(st + 2 < nstages ? st + 2 : nstages - 1, sl_after);
+      uint4 vnext[kPer];
+      fetch(sl_next, vnext);
+      const int nu = min(4, (kv_end - kStageTok * st + 15) / 16);  // units in this stage
+      for (int u4 = 0; u4 < nu; ++u4) compute(st & 1, 16 * u4, 4 * st + u4);
+      if (st + 1 < nstages) stage_to_lds((st + 1) & 1, vnext);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) sl_next[m] = sl_after[m];
+      __syncthreads();
+    }
+
+    // ---- finalize ----
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      float l = lsum[x] + __shfl_xor(lsum[x], 16, 64);
+      l += __shfl_xor(l, 32, 64);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = 4 * r + jj;
+        const float lc = __shfl(l, col, 64);
+        const int rc = row0 + 16 * x + col;
+        const int i_tok = rc / G, h_in = rc % G;
+        if (i_tok < n) {
+          const float inv = 1.0f / lc;
+          uint16_t* dst = a.out + ((int64_t)(q0 + i_tok) * H + (int64_t)g * G + h_in) * D + VE * c;
+          __bf16 ob[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) ob[e] = (__bf16)(acc[x][e][jj] * inv);
+          if constexpr (VE == 8) *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, ob);
+          else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, ob);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+  if (PD_PREFILL_LDS) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(prefill_lds_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(prefill_lds_kernel<128>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(prefill_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(prefill_kernel<128>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
