@@ -106,7 +106,9 @@ typedef struct pd_layout {
   size_t qo_indptr;   /* int32 [max_batch + 1]: extend bind: prefix sum of the
                          new-token counts (prefill query rows)                 */
   size_t item_indptr; /* int32 [max_batch + 1]: extend bind: prefix sum of the
-                         prefill work items per request                        */
+                         prefill work items per request, in req_order          */
+  size_t req_order;   /* int32 [max_batch]: extend bind: requests by decreasing
+                         length (the prefill schedule)                         */
   size_t meta;        /* int32 [16]: [0] = max pages of any request this step,
                          [1] = total tokens, [2] = total pages this step       */
   size_t error_word;  /* uint32: PD_ERR_* bits                                 */

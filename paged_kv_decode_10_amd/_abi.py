@@ -64,7 +64,7 @@ class PdConfig(ctypes.Structure):
 class PdLayout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_size_t) for name in (
         "arena_bytes", "kv_indptr", "kv_indices", "page_indptr", "o_part", "ml_part", "qo_indptr", "item_indptr",
-        "meta", "error_word")]
+        "req_order", "meta", "error_word")]
 
 
 class PdStepBuffers(ctypes.Structure):

@@ -95,8 +95,13 @@ bind_scan_kernel(BindArgs a) {
   }
   if (a.extend_lens != nullptr) {
     // Extend / prefill: the last n_b of the (clipped) tokens are new, one
-    // query row each; qo_indptr is the prefix sum of n_b, and item_indptr that
-    // of the work items n_kv_heads * ceil(n_b * group / kPrefillRows).
+    // query row each; qo_indptr is the prefix sum of n_b.  The prefill work
+    // items (n_kv_heads * ceil(n_b * group / kPrefillRows) per request) are
+    // listed request by request in order of decreasing length (req_order;
+    // item_indptr is their prefix sum in that order), so the long items come
+    // first in the prefill's schedule.
+    __shared__ int32_t s_key[kScanThreads];
+    __shared__ int32_t s_idx[kScanThreads];
     int64_t nb = 0;
     if (b < B) {
       nb = a.extend_lens[b];
@@ -105,28 +110,56 @@ bind_scan_kernel(BindArgs a) {
     }
     const int64_t items = (int64_t)a.n_kv_heads * ((nb * a.group + kPrefillRows - 1) / kPrefillRows);
     const int64_t qincl = wave_inclusive_scan(nb);
-    const int64_t iincl = wave_inclusive_scan(items);
     __syncthreads();  // wave_tot is reused
     if (lane == 63) wave_tot[wave] = qincl;
     __syncthreads();
     int64_t qbefore = 0;
     for (int w = 0; w < wave; ++w) qbefore += wave_tot[w];
+    if (b < B) {
+      a.qo_indptr[b + 1] = (int32_t)(qbefore + qincl);
+      if (b == 0) a.qo_indptr[0] = 0;
+      if (b == B - 1) a.meta[kMetaTotalQ] = (int32_t)(qbefore + qincl);
+    }
+    // Bitonic sort of (length, request) over the block: descending length,
+    // ascending request on ties; requests without items and padding last.
+    s_key[b] = (b < B && items > 0) ? (int32_t)(hi - lo) : -1;
+    s_idx[b] = b;
+    __syncthreads();
+    for (int size = 2; size <= kScanThreads; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const int partner = b ^ stride;
+        if (partner > b) {
+          const bool first_block = (b & size) == 0;  // this half is sorted "first-before-second"
+          const int32_t k0 = s_key[b], k1 = s_key[partner];
+          const int32_t i0 = s_idx[b], i1 = s_idx[partner];
+          const bool before = (k0 > k1) || (k0 == k1 && i0 < i1);  // (k0, i0) goes first
+          if (before != first_block) {
+            s_key[b] = k1; s_key[partner] = k0;
+            s_idx[b] = i1; s_idx[partner] = i0;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // thread p now holds the p-th request of the schedule
+    const int rb = s_idx[b];
+    __syncthreads();
+    // items of request rb, counted by the thread that owns rb
+    __shared__ int32_t s_items[kScanThreads];
+    s_items[b] = (int32_t)items;
+    __syncthreads();
+    const int64_t my_items = (b < B) ? s_items[rb] : 0;
+    const int64_t iincl = wave_inclusive_scan(my_items);
     __syncthreads();
     if (lane == 63) wave_tot[wave] = iincl;
     __syncthreads();
     int64_t ibefore = 0;
     for (int w = 0; w < wave; ++w) ibefore += wave_tot[w];
     if (b < B) {
-      a.qo_indptr[b + 1] = (int32_t)(qbefore + qincl);
       a.item_indptr[b + 1] = (int32_t)(ibefore + iincl);
-      if (b == 0) {
-        a.qo_indptr[0] = 0;
-        a.item_indptr[0] = 0;
-      }
-      if (b == B - 1) {
-        a.meta[kMetaTotalQ] = (int32_t)(qbefore + qincl);
-        a.meta[kMetaTotalItems] = (int32_t)(ibefore + iincl);
-      }
+      a.req_order[b] = rb;
+      if (b == 0) a.item_indptr[0] = 0;
+      if (b == B - 1) a.meta[kMetaTotalItems] = (int32_t)(ibefore + iincl);
     }
   }
   if (flags) atomicOr(a.error_word, flags);

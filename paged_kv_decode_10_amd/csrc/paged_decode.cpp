@@ -58,6 +58,8 @@ pd_layout make_layout(const pd_config* c) {
   off = align_up(off + (size_t)(c->max_batch + 1) * 4);
   l.item_indptr = off;
   off = align_up(off + (size_t)(c->max_batch + 1) * 4);
+  l.req_order = off;
+  off = align_up(off + (size_t)c->max_batch * 4);
   l.meta = off;
   off = align_up(off + 16 * 4);
   l.error_word = off;
@@ -109,6 +111,7 @@ pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena, size_
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.meta, 0, 16 * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.qo_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.item_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
+  if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.req_order, 0, (size_t)cfg->max_batch * 4, nullptr);
   if (e == hipSuccess) e = hipMemsetAsync(h->arena + lay.error_word, 0, 4, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) {
@@ -185,6 +188,7 @@ pd_status pdh::bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d
     a.extend_lens = d_extend_lens;
     a.qo_indptr = at<int32_t>(h, h->lay.qo_indptr);
     a.item_indptr = at<int32_t>(h, h->lay.item_indptr);
+    a.req_order = at<int32_t>(h, h->lay.req_order);
     a.group = h->cfg.n_heads / h->cfg.n_kv_heads;
     a.n_kv_heads = h->cfg.n_kv_heads;
   }
@@ -319,7 +323,9 @@ pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, 
   a.qo_indptr = at<int32_t>(h, h->lay.qo_indptr);
   a.error_word = at<uint32_t>(h, h->lay.error_word);
   a.item_indptr = at<int32_t>(h, h->lay.item_indptr);
+  a.req_order = at<int32_t>(h, h->lay.req_order);
   a.meta = at<int32_t>(h, h->lay.meta);
+  a.claim = at<int32_t>(h, h->lay.meta) + pd::kMetaPrefillClaim;
   a.out = static_cast<uint16_t*>(d_out);
   return hip_status(pd::launch_prefill(a, c.head_dim, stream));
 }

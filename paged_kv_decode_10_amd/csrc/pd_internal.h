@@ -17,6 +17,7 @@ enum MetaWord : int {
   kMetaActive = 4,       // active requests of a padded graph-pool step (graph pool only)
   kMetaTotalQ = 5,       // extend bind: sum of the (clamped) new-token counts
   kMetaTotalItems = 6,   // extend bind: prefill work items (request, kv head, query rows)
+  kMetaPrefillClaim = 7, // prefill: work-item counter (0 between launches)
 };
 
 // The attention launches this many waves.  They work in teams of
@@ -62,7 +63,8 @@ struct BindArgs {
   // (n_kv_heads * ceil(n_b * group / kPrefillRows)).
   const int32_t* extend_lens;
   int32_t* qo_indptr;
-  int32_t* item_indptr;
+  int32_t* item_indptr;       // over the requests in req_order
+  int32_t* req_order;         // requests by decreasing length (prefill schedule)
   int32_t group;
   int32_t n_kv_heads;
 };
@@ -147,7 +149,9 @@ struct PrefillArgs {
   const int32_t* kv_indices;
   const int32_t* qo_indptr;
   const int32_t* item_indptr;
+  const int32_t* req_order;
   const int32_t* meta;
+  int32_t* claim;             // the work-item counter (a meta word)
   uint16_t* out;              // bf16 [q_rows, n_heads, D]
   uint32_t* error_word;
 };

@@ -105,12 +105,13 @@ prefill_kernel(PrefillArgs a) {
       const bool le = i <= B && a.item_indptr[i <= B ? i : B] <= item;
       cnt += __popcll(__builtin_amdgcn_ballot_w64(le));
     }
-    const int b = __builtin_amdgcn_readfirstlane(cnt - 1);
-    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[b]);
-    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[b + 1]);
+    const int pos = __builtin_amdgcn_readfirstlane(cnt - 1);  // place of the request in the schedule
+    const int b = __builtin_amdgcn_readfirstlane(a.req_order[pos]);
+    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[pos]);
+    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[pos + 1]);
     const int groups = (i_hi - i_lo) / Hkv;  // items per kv head
-    const int k = item - i_lo;
-    const int g = k / groups, grp = k % groups;
+    const int k = item - i_lo;  // the request's row groups last-first (longest causal range first)
+    const int g = k % Hkv, grp = groups - 1 - k / Hkv;
     const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
     const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
     const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
@@ -279,19 +280,30 @@ prefill_lds_kernel(PrefillArgs a) {
   const int total_items = a.meta[kMetaTotalItems];
   const int64_t kv_stride = (int64_t)Hkv * D;
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+  // Schedule: workgroup w first takes item w, then items W + k for k handed out
+  // by the counter (the next claim is requested while an item is computed).
+  // Every workgroup that had a first item ends with exactly one claim past the
+  // end; the one that receives the last index ever handed out resets the
+  // counter for the next launch.
+  __shared__ int32_t s_claim;
+  const int W = gridDim.x;
+  const int last_claim = max(total_items - W, 0) + min(total_items, W) - 1;
+  for (int item = blockIdx.x; item < total_items;) {
+    int32_t kc = 0;
+    if (tid == 0) kc = __hip_atomic_fetch_add(a.claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int cnt = 0;
     for (int i0 = 0; i0 <= B; i0 += 64) {
       const int i = i0 + lane;
       const bool le = i <= B && a.item_indptr[i <= B ? i : B] <= item;
       cnt += __popcll(__builtin_amdgcn_ballot_w64(le));
     }
-    const int b = __builtin_amdgcn_readfirstlane(cnt - 1);
-    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[b]);
-    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[b + 1]);
+    const int pos = __builtin_amdgcn_readfirstlane(cnt - 1);  // place of the request in the schedule
+    const int b = __builtin_amdgcn_readfirstlane(a.req_order[pos]);
+    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[pos]);
+    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[pos + 1]);
     const int groups = (i_hi - i_lo) / Hkv;
-    const int k = item - i_lo;
-    const int g = k / groups, grp = k % groups;
+    const int k = item - i_lo;  // the request's row groups last-first (longest causal range first)
+    const int g = k % Hkv, grp = groups - 1 - k / Hkv;
     const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
     const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
     const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
@@ -299,7 +311,8 @@ prefill_lds_kernel(PrefillArgs a) {
     const int n = min(n_all, max(a.q_rows - q0, 0));
     if (n < n_all && tid == 0) atomicOr(a.error_word, PD_ERR_TOTAL_OVER_CAP);
     const int row0_item = kPrefillRows * grp;
-    if (n <= 0 || row0_item >= n * G) continue;  // the whole workgroup skips the item
+    const bool skip = n <= 0 || row0_item >= n * G;  // the whole workgroup skips the item
+    if (!skip) {
     // the item's K/V range (all four waves walk it; rows past their own
     // causal limit are masked)
     const int last_item_tok = min(n - 1, (row0_item + kPrefillRows - 1) / G);
@@ -488,6 +501,15 @@ prefill_lds_kernel(PrefillArgs a) {
         }
       }
     }
+    }  // !skip
+    // ---- next item ----
+    if (tid == 0) s_claim = kc;
+    __syncthreads();
+    kc = s_claim;
+    __syncthreads();  // s_claim is rewritten by the next item
+    item = W + kc;
+    if (item >= total_items && tid == 0 && kc == last_claim)
+      __hip_atomic_store(a.claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

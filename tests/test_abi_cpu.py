@@ -54,10 +54,11 @@ def test_workspace_bytes_and_validation(abi):
     c = _cfg(abi)
     assert L.paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == abi.PD_OK
     rows = 4 * 32 * 8
-    # kv_indptr, kv_indices, page_indptr, o_part, ml_part, qo_indptr, item_indptr, meta, error word, 256-aligned
+    # kv_indptr, kv_indices, page_indptr, o_part, ml_part, qo_indptr, item_indptr, req_order, meta,
+    # error word, each 256-aligned
     al = lambda x: -(-x // 256) * 256
     want = (al(5 * 4) + al(1000 * 4) + al(5 * 4) + al(rows * 128 * 4) + al(rows * 2 * 4) + al(5 * 4) + al(5 * 4)
-            + al(64) + al(4))
+            + al(4 * 4) + al(64) + al(4))
     assert n.value == want
     for bad, code in [(dict(head_dim=96), abi.PD_E_UNSUPPORTED), (dict(n_heads=30), abi.PD_E_UNSUPPORTED),
                       (dict(n_heads=8 * 17), abi.PD_E_UNSUPPORTED), (dict(page_size=0), abi.PD_E_INVALID),

@@ -136,3 +136,38 @@ def test_extend_over_length_is_flagged():
     torch.cuda.synchronize()
     assert ws.read_error() & PD_ERR_EXTEND_OVER_LEN
     assert ws.qo_indptr[:3].cpu().tolist() == [0, 20, 30]
+
+
+def test_prefill_repeated_launches_bit_identical():
+    """Items are handed out dynamically; the result must not depend on the
+    schedule, and the work counter must be back at zero after every launch
+    (else a later launch would skip items and leave NaN rows)."""
+    w = workloads.make("prefill")
+    dev = to_device(w)
+    ws = make_ws(w)
+    ws.bind_extend(w.batch, dev.seq_lens, w.meta["extend_lens"].cuda(), req_to_page=dev.req_to_page)
+    outs = []
+    for _ in range(4):
+        out = torch.full(dev.q[0].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        ws.prefill_attn(w.batch, 0, dev.q[0], dev.k, dev.v, w.scale, out)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).cpu())
+    assert torch.isfinite(outs[0].view(torch.bfloat16).float()).all()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    # a second bind with a different mix reuses the counter
+    ext2 = (w.meta["extend_lens"] // 2).cuda()
+    ws.bind_extend(w.batch, dev.seq_lens, ext2, req_to_page=dev.req_to_page)
+    rows = int(ext2.sum())
+    out = torch.full((rows, w.n_heads, w.head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+    # the new tokens are the last n_b/2 of each request: their query rows
+    qrows = torch.cat([dev.q[0][int(s) - int(e):int(s)] for s, e in
+                       zip(torch.cumsum(w.meta["extend_lens"], 0), ext2.cpu())]).contiguous()
+    ws.prefill_attn(w.batch, 0, qrows, dev.k, dev.v, w.scale, out)
+    torch.cuda.synchronize()
+    assert ws.read_error() == 0
+    L = w.seq_lens.numpy()
+    ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+    ref, _ = oracle.prefill_attention(qrows.cpu(), w.k_store[0], w.v_store[0], L, ext2.cpu().numpy(), ip, ix,
+                                      w.scale, w.n_kv_heads)
+    assert_close_out(out.float().cpu().numpy(), ref, "prefill after a rebind")
