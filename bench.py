@@ -390,6 +390,14 @@ def main() -> int:
     if args.configs:
         rows = config_sweep([x for x in args.configs.split(",") if x], args.config_reps, args.oracle_budget,
                             args.splits)
+        if args.calib_copy_gib > 0:  # a plain copy of known size, for counter calibration
+            n = int(args.calib_copy_gib * (1 << 30))
+            src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         print(json.dumps({"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "data": "synthetic", "dtype": "bf16",
                           "timing": "HIP events per launch, 1 GiB flush-write before each iteration",
                           "configs": rows}), flush=True)
