@@ -509,8 +509,20 @@ split_attn_kernel(AttnArgs a) {
   Tile<D> TA = load_tile<D, APPEND>(a, uA, GP, r, c);
   Tile<D> TB = load_tile<D, APPEND>(a, uB, GP, r, c);
   int nunits = 0;
+  // The two workgroups sharing a CU: the wave arbiter favours the older one,
+  // which then finishes ~20% earlier.  The later-dispatched workgroup (second
+  // half of the grid) raises its priority for the first half of its units and
+  // the earlier one for the second half, so each is favoured for half its
+  // life.  Priority only changes timing, never results.
+  const bool young = blockIdx.x >= gridDim.x / 2;
+  const int half = (int)((row_mode ? 1 : pr.Qp) * pr.upp / 2);
+  if (young) __builtin_amdgcn_s_setprio(1);
   while (uA.valid) {
     compute(TA, uA);
+    if (nunits == half) {
+      if (young) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(1);
+    }
     if (nunits++ == 0) PD_STAMP(2, wall_clock64());
     TA = load_tile<D, APPEND>(a, uC, GP, r, c);
     uA = uC;
