@@ -259,7 +259,7 @@ def prefill_bench(name: str, reps: int):
     """Prefill / extend attention on a prefill workload, one launch at a time
     with the caches flushed: HIP-event median, algorithmic flops (QK^T and PV
     over each query's causal range) and the K/V bytes the kernel streams
-    (every work item of 32 query rows reads its causal range once)."""
+    (every work item of 128 query rows reads its causal range once)."""
     import numpy as np
     import torch
 
@@ -294,7 +294,7 @@ def prefill_bench(name: str, reps: int):
     n = w.meta["extend_lens"].numpy().astype(np.int64)
     keys = sum(int(((L[b] - n[b]) + np.arange(n[b]) + 1).sum()) for b in range(B))  # causal key count per query
     flops = 4 * D * H * keys  # 2 flops per MAC, QK^T and PV
-    rows = 32  # query rows per work item of the library's prefill kernel
+    rows = 128  # query rows per work item of the library's prefill kernel (4 waves x 32)
     streamed = 0
     for b in range(B):
         for t in range(-(-int(n[b]) * G // rows)):

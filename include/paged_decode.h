@@ -234,7 +234,8 @@ pd_status paged_decode_bind_extend(pd_handle* h, int32_t batch, int32_t* d_seq_l
  *           it (sum n_b > q_rows) are not computed and set PD_ERR_TOTAL_OVER_CAP
  *   d_out   bf16 [q_rows, n_heads, head_dim], caller-owned
  *   stores as in paged_decode_attn.  Reads the last extend bind.  One
- * persistent launch (2048 waves over (request, kv head, 32 query rows)). */
+ * persistent launch: 512 workgroups of 4 waves over work items (request,
+ * kv head, 128 query rows), longest requests first. */
 pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q, int32_t q_rows,
                                     const void* d_k_store, const void* d_v_store, float scale, void* d_out,
                                     hipStream_t stream);
