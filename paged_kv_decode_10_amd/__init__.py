@@ -241,6 +241,16 @@ class PagedDecode:
     def qo_indptr(self):
         return self._view(self.layout["qo_indptr"], torch.int32, (self.cfg.max_batch + 1,))
 
+    @property
+    def item_indptr(self):
+        """Extend bind: prefix sum of the prefill work items, in schedule order."""
+        return self._view(self.layout["item_indptr"], torch.int32, (self.cfg.max_batch + 1,))
+
+    @property
+    def req_order(self):
+        """Extend bind: the requests in schedule order (decreasing length)."""
+        return self._view(self.layout["req_order"], torch.int32, (self.cfg.max_batch,))
+
     def merge(self, batch: int, num_splits: int, out: torch.Tensor, stream=None) -> None:
         c = self.cfg
         p_o = _dev_ptr(out, torch.bfloat16, "out", batch * c.n_heads * c.head_dim)

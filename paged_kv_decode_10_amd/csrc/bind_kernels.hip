@@ -120,12 +120,15 @@ bind_scan_kernel(BindArgs a) {
       if (b == 0) a.qo_indptr[0] = 0;
       if (b == B - 1) a.meta[kMetaTotalQ] = (int32_t)(qbefore + qincl);
     }
-    // Bitonic sort of (length, request) over the block: descending length,
-    // ascending request on ties; requests without items and padding last.
+    // Bitonic sort of (length, request) over the first P2 = 2^ceil(log2 B)
+    // entries: descending length, ascending request on ties; requests without
+    // items and padding last.  Entries from P2 on are padding and stay put.
     s_key[b] = (b < B && items > 0) ? (int32_t)(hi - lo) : -1;
     s_idx[b] = b;
+    int P2 = 1;
+    while (P2 < B) P2 <<= 1;
     __syncthreads();
-    for (int size = 2; size <= kScanThreads; size <<= 1) {
+    for (int size = 2; size <= P2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         const int partner = b ^ stride;
         if (partner > b) {

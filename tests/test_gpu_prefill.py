@@ -171,3 +171,36 @@ def test_prefill_repeated_launches_bit_identical():
     ref, _ = oracle.prefill_attention(qrows.cpu(), w.k_store[0], w.v_store[0], L, ext2.cpu().numpy(), ip, ix,
                                       w.scale, w.n_kv_heads)
     assert_close_out(out.float().cpu().numpy(), ref, "prefill after a rebind")
+
+
+@pytest.mark.parametrize("B", [1, 2, 5, 16, 33, 1000])
+def test_extend_bind_schedule(B):
+    """The extend bind's work list: qo_indptr is the prefix sum of the clamped
+    new-token counts; req_order lists the requests with work by decreasing
+    length (ties by index), then the rest by index; item_indptr is the prefix
+    sum, in that order, of n_kv_heads * ceil(n_b * G / 128) items."""
+    from paged_kv_decode_10_amd import Config, PagedDecode
+
+    say(f"[extend bind] B={B}")
+    rng = np.random.default_rng(500 + B)
+    H, Hkv, D, ps, cap = 32, 8, 128, 16, 64 * 16
+    L = rng.integers(0, cap + 1, size=B)
+    L[rng.random(B) < 0.2] = int(rng.integers(0, cap + 1))  # ties
+    n = np.minimum(rng.integers(0, 300, size=B), L)
+    n[rng.random(B) < 0.1] = 0  # requests without new tokens
+    cfg = Config(n_layers=1, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=ps, max_batch=B, max_splits=4,
+                 max_pages_per_req=cap // ps, num_slots=B * cap, max_total_tokens=int(L.sum()) + 1)
+    ws = PagedDecode(cfg)
+    seq = torch.from_numpy(L.astype(np.int32)).cuda()
+    ext = torch.from_numpy(n.astype(np.int32)).cuda()
+    base = torch.arange(B, dtype=torch.int32, device="cuda") * cap
+    ws.bind_extend(B, seq, ext, req_base=base)
+    torch.cuda.synchronize()
+    assert ws.read_error() == 0
+    items = Hkv * -(-(n * (H // Hkv)) // 128)
+    want_qo = np.concatenate([[0], np.cumsum(n)])
+    order = sorted(range(B), key=lambda b: (0, -int(L[b]), b) if items[b] > 0 else (1, 0, b))
+    want_items = np.concatenate([[0], np.cumsum(items[order])])
+    assert np.array_equal(ws.qo_indptr[: B + 1].cpu().numpy(), want_qo)
+    assert ws.req_order[:B].cpu().numpy().tolist() == order
+    assert np.array_equal(ws.item_indptr[: B + 1].cpu().numpy(), want_items)
