@@ -409,23 +409,37 @@ prefill_lds_kernel(PrefillArgs a) {
           bv[e][1] = __builtin_amdgcn_perm(pick(vr[3]), pick(vr[2]), sel);
         }
       }
+      // Scores of both tiles first (independent MFMA chains), then one
+      // wave-uniform check whether any row's reference max must move.
+      f32x4_t sc[NQ];
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) sc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int x = 0; x < NQ; ++x)
+          sc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                          __builtin_bit_cast(bf16x8_t, qv[x][s]), sc[x], 0, 0, 0);
+      float t[NQ][4];
+      bool need[NQ];
 #pragma unroll
       for (int x = 0; x < NQ; ++x) {
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
-                                                       __builtin_bit_cast(bf16x8_t, qv[x][s]), sc, 0, 0, 0);
-        float t[4];
-        bool need = false;
+        need[x] = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * u + 4 * r + i;
-          t[i] = (tok <= pos_c[x] && tok < kv_end) ? sc[i] * a.scale_log2 : -INFINITY;
-          need |= t[i] > mref[x] + kSlack;
+          t[x][i] = (tok <= pos_c[x] && tok < kv_end) ? sc[x][i] * a.scale_log2 : -INFINITY;
+          need[x] |= t[x][i] > mref[x] + kSlack;
         }
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          float cm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+      }
+      bool any = false;
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) any |= need[x];
+      if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+        for (int x = 0; x < NQ; ++x) {
+          if (!__builtin_amdgcn_ballot_w64(need[x])) continue;
+          float cm = fmaxf(fmaxf(t[x][0], t[x][1]), fmaxf(t[x][2], t[x][3]));
           cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
           cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
           const float mnew = fmaxf(mref[x], cm);
@@ -439,10 +453,13 @@ prefill_lds_kernel(PrefillArgs a) {
             for (int e = 0; e < VE; ++e) acc[x][e][jj] *= ar;
           }
         }
+      }
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) {
         bf16x4_t pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = t[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[i] - mref[x]);
+          const float p = t[x][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[x][i] - mref[x]);
           lsum[x] += p;
           pb[i] = (__bf16)p;
         }
