@@ -377,12 +377,9 @@ prefill_lds_kernel(PrefillArgs a) {
       lsum[x] = 0.f;
     }
 
-    // 16-token unit `u` (absolute) whose rows start at row t0 of LDS buffer `buf`
-    auto compute = [&](int buf, int t0, int u) {
-      uint4 kk[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kk[s] = sK[buf][(t0 + c) * RS + r + 4 * s];  // token c, bytes 16r + 64s
-      u32x2_t bv[VE];
+    // V operand of the 16-token unit whose rows start at row t0 of LDS buffer
+    // buf: lane (r, c) packs element e of chunk c of tokens 4r .. 4r+3
+    auto v_operand = [&](int buf, int t0, u32x2_t (&bv)[VE]) {
       if constexpr (VE == 8) {
         uint4 vr[4];
 #pragma unroll
@@ -409,28 +406,46 @@ prefill_lds_kernel(PrefillArgs a) {
           bv[e][1] = __builtin_amdgcn_perm(pick(vr[3]), pick(vr[2]), sel);
         }
       }
-      // Scores of both tiles first (independent MFMA chains), then one
-      // wave-uniform check whether any row's reference max must move.
-      f32x4_t sc[NQ];
+    };
+
+    // One 64-token stage (LDS buffer buf, tokens 64*st ...): the scores of its
+    // four 16-token units for both tiles, one wave-uniform check whether a
+    // row's reference max must move, then p = exp2(s - mref) and p.V two
+    // units at a time.  p.V runs on the 16x16x32 MFMA: lane (r, c) holds p of
+    // query row c for tokens 4r..4r+3 of the first unit and of the second in
+    // its eight k slots, and the V operand lists the same tokens in the same
+    // order, so the k order is a permutation that the sum does not see.  Rows
+    // of the stage past kv_end hold copies of the last token (the staging
+    // clamps them) and are masked, so a short last stage needs no branch.
+    auto compute_stage = [&](int buf, int st) {
+      f32x4_t t[4][NQ];  // scores, then scaled and masked (log2 units)
 #pragma unroll
-      for (int x = 0; x < NQ; ++x) sc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int uu = 0; uu < 4; ++uu) {
+        uint4 kk[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) kk[s] = sK[buf][(16 * uu + c) * RS + r + 4 * s];  // token c of unit uu
 #pragma unroll
-        for (int x = 0; x < NQ; ++x)
-          sc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
-                                                          __builtin_bit_cast(bf16x8_t, qv[x][s]), sc[x], 0, 0, 0);
-      float t[NQ][4];
+        for (int x = 0; x < NQ; ++x) t[uu][x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int x = 0; x < NQ; ++x)
+            t[uu][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                               __builtin_bit_cast(bf16x8_t, qv[x][s]), t[uu][x], 0,
+                                                               0, 0);
+      }
       bool need[NQ];
 #pragma unroll
       for (int x = 0; x < NQ; ++x) {
         need[x] = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * u + 4 * r + i;
-          t[x][i] = (tok <= pos_c[x] && tok < kv_end) ? sc[x][i] * a.scale_log2 : -INFINITY;
-          need[x] |= t[x][i] > mref[x] + kSlack;
-        }
+        for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = kStageTok * st + 16 * uu + 4 * r + i;
+            t[uu][x][i] = (tok <= pos_c[x] && tok < kv_end) ? t[uu][x][i] * a.scale_log2 : -INFINITY;
+            need[x] |= t[uu][x][i] > mref[x] + kSlack;
+          }
       }
       bool any = false;
 #pragma unroll
@@ -439,7 +454,10 @@ prefill_lds_kernel(PrefillArgs a) {
 #pragma unroll
         for (int x = 0; x < NQ; ++x) {
           if (!__builtin_amdgcn_ballot_w64(need[x])) continue;
-          float cm = fmaxf(fmaxf(t[x][0], t[x][1]), fmaxf(t[x][2], t[x][3]));
+          float cm = -INFINITY;
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu)
+            cm = fmaxf(cm, fmaxf(fmaxf(t[uu][x][0], t[uu][x][1]), fmaxf(t[uu][x][2], t[uu][x][3])));
           cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
           cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
           const float mnew = fmaxf(mref[x], cm);
@@ -454,20 +472,40 @@ prefill_lds_kernel(PrefillArgs a) {
           }
         }
       }
+      // p for every unit and tile, packed to bf16 (the scores die here)
+      bf16x4_t pk[4][NQ];
 #pragma unroll
-      for (int x = 0; x < NQ; ++x) {
-        bf16x4_t pb;
+      for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = t[x][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[x][i] - mref[x]);
-          lsum[x] += p;
-          pb[i] = (__bf16)p;
+        for (int x = 0; x < NQ; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float tv = t[uu][x][i];
+            const float p = tv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(tv - mref[x]);
+            lsum[x] += p;
+            pk[uu][x][i] = (__bf16)p;
+          }
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        bf16x8_t pa[NQ];
+#pragma unroll
+        for (int x = 0; x < NQ; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pa[x][i] = pk[2 * pr][x][i];
+            pa[x][4 + i] = pk[2 * pr + 1][x][i];
+          }
+        u32x2_t bv0[VE], bv1[VE];
+        v_operand(buf, 32 * pr, bv0);
+        v_operand(buf, 32 * pr + 16, bv1);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const uint4 b = make_uint4(bv0[e][0], bv0[e][1], bv1[e][0], bv1[e][1]);
+#pragma unroll
+          for (int x = 0; x < NQ; ++x)
+            acc[x][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[x], __builtin_bit_cast(bf16x8_t, b), acc[x][e], 0,
+                                                                0, 0);
         }
-        const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-          acc[x][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv[e]), acc[x][e],
-                                                                 0, 0, 0);
       }
     };
 
@@ -488,8 +526,7 @@ prefill_lds_kernel(PrefillArgs a) {
       slots_of(st + 2 < nstages ? st + 2 : nstages - 1, sl_after);
       uint4 vnext[kPer];
       fetch(sl_next, vnext);
-      const int nu = min(4, (kv_end - kStageTok * st + 15) / 16);  // units in this stage
-      for (int u4 = 0; u4 < nu; ++u4) compute(st & 1, 16 * u4, 4 * st + u4);
+      compute_stage(st & 1, st);
       if (st + 1 < nstages) stage_to_lds((st + 1) & 1, vnext);
 #pragma unroll
       for (int m = 0; m < kPer; ++m) sl_next[m] = sl_after[m];
