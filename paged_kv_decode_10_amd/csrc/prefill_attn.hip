@@ -321,13 +321,14 @@ prefill_lds_kernel(PrefillArgs a) {
     const int row0 = row0_item + 16 * NQ * wv;  // this wave's rows
 
     uint4 qv[NQ][KS];
-    int pos_c[NQ];
+    int pos_c[NQ], pos_lo[NQ];
 #pragma unroll
     for (int x = 0; x < NQ; ++x) {
       const int rc = row0 + 16 * x + c;
       const int ic = rc / G, hh = rc % G;
       const bool valid = ic < n;
       pos_c[x] = L - n_all + ic;
+      pos_lo[x] = __builtin_amdgcn_readfirstlane(L - n_all + (row0 + 16 * x) / G);  // the tile's smallest causal limit
       const uint16_t* qp =
           a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
 #pragma unroll
@@ -434,18 +435,35 @@ prefill_lds_kernel(PrefillArgs a) {
                                                                __builtin_bit_cast(bf16x8_t, qv[x][s]), t[uu][x], 0,
                                                                0, 0);
       }
-      bool need[NQ];
+      // A stage wholly inside the item's range and below both tiles' causal
+      // diagonals needs no mask (the common case).
+      const int last_tok = kStageTok * st + kStageTok - 1;
+      bool full = last_tok < kv_end;
 #pragma unroll
-      for (int x = 0; x < NQ; ++x) {
-        need[x] = false;
+      for (int x = 0; x < NQ; ++x) full = full && last_tok <= pos_lo[x];
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+        for (int x = 0; x < NQ; ++x) t[uu][x] *= a.scale_log2;
+      if (!full) {
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = kStageTok * st + 16 * uu + 4 * r + i;
-            t[uu][x][i] = (tok <= pos_c[x] && tok < kv_end) ? t[uu][x][i] * a.scale_log2 : -INFINITY;
-            need[x] |= t[uu][x][i] > mref[x] + kSlack;
-          }
+          for (int x = 0; x < NQ; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tok = kStageTok * st + 16 * uu + 4 * r + i;
+              if (!(tok <= pos_c[x] && tok < kv_end)) t[uu][x][i] = -INFINITY;
+            }
+      }
+      bool need[NQ];
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu)
+          mx = fmaxf(mx, fmaxf(fmaxf(t[uu][x][0], t[uu][x][1]), fmaxf(t[uu][x][2], t[uu][x][3])));
+        need[x] = mx > mref[x] + kSlack;
       }
       bool any = false;
 #pragma unroll
@@ -472,7 +490,9 @@ prefill_lds_kernel(PrefillArgs a) {
           }
         }
       }
-      // p for every unit and tile, packed to bf16 (the scores die here)
+      // p for every unit and tile, packed to bf16 (the scores die here).
+      // mref is finite here: token 0 is visible to every row, so the first
+      // stage set it, and a masked score gives exp2(-inf) = 0.
       bf16x4_t pk[4][NQ];
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu)
@@ -480,8 +500,7 @@ prefill_lds_kernel(PrefillArgs a) {
         for (int x = 0; x < NQ; ++x)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float tv = t[uu][x][i];
-            const float p = tv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(tv - mref[x]);
+            const float p = __builtin_amdgcn_exp2f(t[uu][x][i] - mref[x]);
             lsum[x] += p;
             pk[uu][x][i] = (__bf16)p;
           }
