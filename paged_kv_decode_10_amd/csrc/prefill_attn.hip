@@ -262,6 +262,22 @@ prefill_kernel(PrefillArgs a) {
 // round trip covers four units of compute.
 constexpr int kStageTok = 64;
 
+// One token's V values for one lane column group: VE bf16 (16 or 8 bytes).
+template <int VE>
+struct VPiece;
+template <>
+struct VPiece<8> {
+  uint4 u;
+  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w; }
+  __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+};
+template <>
+struct VPiece<4> {
+  uint2 u;
+  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : u.y; }
+  __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+};
+
 template <int D>
 __global__ void __launch_bounds__(kThreads, PD_PREFILL_WAVES_PER_SIMD)
 prefill_lds_kernel(PrefillArgs a) {
@@ -269,10 +285,15 @@ prefill_lds_kernel(PrefillArgs a) {
   constexpr int NQ = kPrefillTiles;
   constexpr int CPR = D / 8;                          // 16-byte chunks per K or V row
   constexpr int RS = CPR + 1;                         // padded LDS row stride (uint4)
-  constexpr int kStageChunks = kStageTok * CPR;       // per tensor
-  constexpr int kPer = 2 * kStageChunks / kThreads;   // chunks a thread moves per stage (K then V)
+  constexpr int kStageChunks = kStageTok * CPR;       // K chunks per stage
+  constexpr int kKPer = kStageChunks / kThreads;      // K chunks a thread moves per stage
+  constexpr int kPer = kKPer + 4;                     // slots a thread needs per stage (K chunks, 4 V tokens)
+  // K: [token][chunk], rows padded.  V: transposed for the p.V operand --
+  // word (pair p, element e, lane 16r + c) holds element e of lane column
+  // group c for tokens 4r..4r+3 of the pair's first unit, then of its second
+  // (eight bf16, the B operand of one 16x16x32 MFMA), written at staging.
   __shared__ uint4 sK[2][kStageTok * RS];
-  __shared__ uint4 sV[2][kStageTok * RS];
+  __shared__ uint4 sVt[2][2 * VE * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int r = lane >> 4, c = lane & 15;
@@ -338,33 +359,49 @@ prefill_lds_kernel(PrefillArgs a) {
         qv[x][s] = v;
       }
     }
-    // Chunk m of this thread in a stage: index tid + kThreads*m over [K chunks | V chunks];
-    // its token is (index mod kStageChunks) / CPR.
-    auto chunk_tok = [&](int m) { return ((tid + kThreads * m) % kStageChunks) / CPR; };
+    // A thread moves, per stage, K chunks tid + kThreads*m (token index / CPR,
+    // chunk index % CPR), and the V values of lane column group vc for the
+    // four tokens 16*vu + 4*vr + i of unit vu.  Tokens past kv_end are read as
+    // the last token (they are masked).
+    const int vu = tid >> 6, vr = (tid >> 4) & 3, vc = tid & 15;
+    auto tok_of = [&](int m) { return m < kKPer ? (tid + kThreads * m) / CPR : 16 * vu + 4 * vr + (m - kKPer); };
     auto slots_of = [&](int st, int32_t (&sl)[kPer]) {
 #pragma unroll
       for (int m = 0; m < kPer; ++m) {
-        int t = kStageTok * st + chunk_tok(m);
+        int t = kStageTok * st + tok_of(m);
         t = t < kv_end ? t : kv_end - 1;
         sl[m] = a.kv_indices[kv0 + t];
       }
     };
-    auto fetch = [&](const int32_t (&sl)[kPer], uint4 (&v)[kPer]) {
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        const int idx = tid + kThreads * m;
-        const uint16_t* src = (idx < kStageChunks ? a.k_layer : a.v_layer);
-        const int ch = (idx % kStageChunks) % CPR;
-        v[m] = *reinterpret_cast<const uint4*>(src + (int64_t)sl[m] * kv_stride + (int64_t)g * D + 8 * ch);
-      }
+    struct Staged {
+      uint4 k[kKPer];
+      VPiece<VE> v[4];
     };
-    auto stage_to_lds = [&](int buf, const uint4 (&v)[kPer]) {
+    auto fetch = [&](const int32_t (&sl)[kPer], Staged& d) {
 #pragma unroll
-      for (int m = 0; m < kPer; ++m) {
+      for (int m = 0; m < kKPer; ++m) {
+        const int ch = (tid + kThreads * m) % CPR;
+        d.k[m] = *reinterpret_cast<const uint4*>(a.k_layer + (int64_t)sl[m] * kv_stride + (int64_t)g * D + 8 * ch);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d.v[i].load(a.v_layer + (int64_t)sl[kKPer + i] * kv_stride + (int64_t)g * D + VE * vc);
+    };
+    auto stage_to_lds = [&](int buf, const Staged& d) {
+#pragma unroll
+      for (int m = 0; m < kKPer; ++m) {
         const int idx = tid + kThreads * m;
-        const int loc = idx % kStageChunks;
-        uint4* dst = idx < kStageChunks ? sK[buf] : sV[buf];
-        dst[(loc / CPR) * RS + loc % CPR] = v[m];
+        sK[buf][(idx / CPR) * RS + idx % CPR] = d.k[m];
+      }
+      // element e of tokens (4vr, 4vr+1) and (4vr+2, 4vr+3), paired by byte permutes
+      uint2* vt = reinterpret_cast<uint2*>(sVt[buf]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int dw = e >> 1;
+        const uint2 w = make_uint2(__builtin_amdgcn_perm(d.v[1].dw(dw), d.v[0].dw(dw), sel),
+                                   __builtin_amdgcn_perm(d.v[3].dw(dw), d.v[2].dw(dw), sel));
+        vt[(((vu >> 1) * VE + e) * 64 + 16 * vr + vc) * 2 + (vu & 1)] = w;
       }
     };
 
@@ -377,37 +414,6 @@ prefill_lds_kernel(PrefillArgs a) {
       mref[x] = -INFINITY;
       lsum[x] = 0.f;
     }
-
-    // V operand of the 16-token unit whose rows start at row t0 of LDS buffer
-    // buf: lane (r, c) packs element e of chunk c of tokens 4r .. 4r+3
-    auto v_operand = [&](int buf, int t0, u32x2_t (&bv)[VE]) {
-      if constexpr (VE == 8) {
-        uint4 vr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = sV[buf][(t0 + 4 * r + i) * RS + c];  // token 4r+i, chunk c
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const int dw = e >> 1;
-          auto pick = [&](const uint4& x) { return dw == 0 ? x.x : dw == 1 ? x.y : dw == 2 ? x.z : x.w; };
-          bv[e][0] = __builtin_amdgcn_perm(pick(vr[1]), pick(vr[0]), sel);
-          bv[e][1] = __builtin_amdgcn_perm(pick(vr[3]), pick(vr[2]), sel);
-        }
-      } else {
-        uint2 vr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)  // token 4r+i, 8 bytes at 8c
-          vr[i] = reinterpret_cast<const uint2*>(&sV[buf][(t0 + 4 * r + i) * RS])[c];
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const int dw = e >> 1;
-          auto pick = [&](const uint2& x) { return dw == 0 ? x.x : x.y; };
-          bv[e][0] = __builtin_amdgcn_perm(pick(vr[1]), pick(vr[0]), sel);
-          bv[e][1] = __builtin_amdgcn_perm(pick(vr[3]), pick(vr[2]), sel);
-        }
-      }
-    };
 
     // One 64-token stage (LDS buffer buf, tokens 64*st ...): the scores of its
     // four 16-token units for both tiles, one wave-uniform check whether a
@@ -514,12 +520,9 @@ prefill_lds_kernel(PrefillArgs a) {
             pa[x][i] = pk[2 * pr][x][i];
             pa[x][4 + i] = pk[2 * pr + 1][x][i];
           }
-        u32x2_t bv0[VE], bv1[VE];
-        v_operand(buf, 32 * pr, bv0);
-        v_operand(buf, 32 * pr + 16, bv1);
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
-          const uint4 b = make_uint4(bv0[e][0], bv0[e][1], bv1[e][0], bv1[e][1]);
+          const uint4 b = sVt[buf][(pr * VE + e) * 64 + lane];
 #pragma unroll
           for (int x = 0; x < NQ; ++x)
             acc[x][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[x], __builtin_bit_cast(bf16x8_t, b), acc[x][e], 0,
@@ -533,7 +536,7 @@ prefill_lds_kernel(PrefillArgs a) {
     int32_t sl_next[kPer];
     {
       int32_t sl0[kPer];
-      uint4 v0[kPer];
+      Staged v0;
       slots_of(0, sl0);
       fetch(sl0, v0);
       stage_to_lds(0, v0);
@@ -543,7 +546,7 @@ prefill_lds_kernel(PrefillArgs a) {
     for (int st = 0; st < nstages; ++st) {
       int32_t sl_after[kPer];
       slots_of(st + 2 < nstages ? st + 2 : nstages - 1, sl_after);
-      uint4 vnext[kPer];
+      Staged vnext;
       fetch(sl_next, vnext);
       compute_stage(st & 1, st);
       if (st + 1 < nstages) stage_to_lds((st + 1) & 1, vnext);
