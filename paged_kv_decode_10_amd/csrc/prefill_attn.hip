@@ -425,7 +425,7 @@ prefill_lds_kernel(PrefillArgs a) {
     // of the stage past kv_end hold copies of the last token (the staging
     // clamps them) and are masked, so a short last stage needs no branch.
     auto compute_stage = [&](int buf, int st) {
-      f32x4_t t[4][NQ];  // scores, then scaled and masked (log2 units)
+      f32x4_t t[4][NQ];  // raw scores (masked ones -inf)
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu) {
         uint4 kk[KS];
@@ -447,10 +447,8 @@ prefill_lds_kernel(PrefillArgs a) {
       bool full = last_tok < kv_end;
 #pragma unroll
       for (int x = 0; x < NQ; ++x) full = full && last_tok <= pos_lo[x];
-#pragma unroll
-      for (int uu = 0; uu < 4; ++uu)
-#pragma unroll
-        for (int x = 0; x < NQ; ++x) t[uu][x] *= a.scale_log2;
+      // (t stays in raw score units: the scale is applied in the max test and
+      // folded into the exponent)
       if (!full) {
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu)
@@ -469,7 +467,7 @@ prefill_lds_kernel(PrefillArgs a) {
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu)
           mx = fmaxf(mx, fmaxf(fmaxf(t[uu][x][0], t[uu][x][1]), fmaxf(t[uu][x][2], t[uu][x][3])));
-        need[x] = mx > mref[x] + kSlack;
+        need[x] = mx * a.scale_log2 > mref[x] + kSlack;
       }
       bool any = false;
 #pragma unroll
@@ -484,7 +482,7 @@ prefill_lds_kernel(PrefillArgs a) {
             cm = fmaxf(cm, fmaxf(fmaxf(t[uu][x][0], t[uu][x][1]), fmaxf(t[uu][x][2], t[uu][x][3])));
           cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
           cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-          const float mnew = fmaxf(mref[x], cm);
+          const float mnew = fmaxf(mref[x], cm * a.scale_log2);
           const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[x] - mnew);
           lsum[x] *= alpha;
           mref[x] = mnew;
@@ -506,7 +504,7 @@ prefill_lds_kernel(PrefillArgs a) {
         for (int x = 0; x < NQ; ++x)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(t[uu][x][i] - mref[x]);
+            const float p = __builtin_amdgcn_exp2f(fmaf(t[uu][x][i], a.scale_log2, -mref[x]));
             lsum[x] += p;
             pk[uu][x][i] = (__bf16)p;
           }
