@@ -126,16 +126,20 @@ def cpu_baseline(w, budget_s: float, num_splits: int):
                       f"BLAS threads {blas}; numpy {np.__version__}"}
 
 
-def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0):
+def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0, in_step: bool = False):
     """Per-config attention and merge timings with the caches flushed.
 
     For each workload: one bind, then ``reps`` iterations of [1 GiB
     flush-write, attn, merge] with HIP events around the attention and the
     merge separately (on the launch stream).  Reports median / p10 / p90 and
-    the KV-only and all-algorithmic rates at the median.  With
-    ``oracle_budget`` > 0 the oracle is timed on the same inputs, one
-    (request, kv head) pair at a time, for at most about that many seconds
-    per config.
+    the KV-only and all-algorithmic rates at the median.  With ``in_step``
+    the workload has two layers and each iteration is [flush, attn + merge
+    of layer 0 (untimed), attn + merge of layer 1 (timed)]: the timed layer
+    reads KV that no launch has touched since the flush, with the step's
+    index lists already read once, as every layer after the first of a
+    decode step does.  With ``oracle_budget`` > 0 the oracle is timed on the
+    same inputs, one (request, kv head) pair at a time, for at most about
+    that many seconds per config.
     """
     import numpy as np
     import torch
@@ -148,7 +152,7 @@ def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0):
     for name in names:
         t0 = time.perf_counter()
         base_name, _, layout = name.partition("@")  # "b16@contiguous": the contiguous-cache layout
-        w = workloads.make(base_name, layout=layout or "paged")
+        w = workloads.make(base_name, layout=layout or "paged", **({"n_layers": 2} if in_step else {}))
         B, H, Hkv, D = w.batch, w.n_heads, w.n_kv_heads, w.head_dim
         cfg = Config(n_layers=w.n_layers, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size,
                      max_batch=B, max_splits=256, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
@@ -164,10 +168,14 @@ def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0):
             ws.bind(B, PD_BIND_FULL, seq, pos, tab)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ta, tm = [], []
+        lt = 1 if in_step else 0  # the timed layer
         for r in range(reps + 2):
             flush.fill_(r)
+            if in_step:
+                ws.attn(B, 0, S, q[0], kst, vst, w.scale)
+                ws.merge(B, S, out)
             ev[0].record()
-            ws.attn(B, 0, S, q[0], kst, vst, w.scale)
+            ws.attn(B, lt, S, q[lt], kst, vst, w.scale)
             ev[1].record()
             ws.merge(B, S, out)
             ev[2].record()
@@ -180,7 +188,8 @@ def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0):
         kv, alg = attn_bytes(L, Hkv, D, B, H, S, w.page_size)
         pa = np.percentile(ta, [50, 10, 90])
         pm = np.percentile(tm, [50, 10, 90])
-        row = {"workload": name, "batch": B, "n_heads": H, "n_kv_heads": Hkv, "head_dim": D,
+        row = {"workload": name, "timing": "in-step (second layer after a flush)" if in_step else "cold (after a flush)",
+               "batch": B, "n_heads": H, "n_kv_heads": Hkv, "head_dim": D,
                "sum_seq_len": int(L.sum()), "num_splits": S,
                "attn_us": {"median": round(pa[0], 2), "p10": round(pa[1], 2), "p90": round(pa[2], 2)},
                "merge_us": {"median": round(pm[0], 2), "p10": round(pm[1], 2), "p90": round(pm[2], 2)},
@@ -351,6 +360,8 @@ def main() -> int:
                          "NAME@contiguous for the contiguous-cache layout) timed one launch at a time with the "
                          "caches flushed; prints one JSON line")
     ap.add_argument("--config-reps", type=int, default=20)
+    ap.add_argument("--in-step", action="store_true",
+                    help="--configs: time the second of two layers after each flush (index lists warm, KV cold)")
     ap.add_argument("--prefill", default="",
                     help="instead of the step: comma-separated prefill workloads (e.g. prefill) timed one launch at "
                          "a time with the caches flushed; prints one JSON line")
@@ -389,7 +400,7 @@ def main() -> int:
         return 0
     if args.configs:
         rows = config_sweep([x for x in args.configs.split(",") if x], args.config_reps, args.oracle_budget,
-                            args.splits)
+                            args.splits, args.in_step)
         if args.calib_copy_gib > 0:  # a plain copy of known size, for counter calibration
             n = int(args.calib_copy_gib * (1 << 30))
             src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
