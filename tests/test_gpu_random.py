@@ -78,3 +78,26 @@ def test_random_prefill(seed):
     ref, _ = oracle.prefill_attention(w.q[0], w.k_store[0], w.v_store[0], L, np.array(ext), ip, ix, w.scale,
                                       w.n_kv_heads)
     assert_close_out(out.float().cpu().numpy(), ref, f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("B,S", [(100, 0), (100, 7), (1024, 0), (1024, 1), (1024, 3)])
+def test_many_requests(B, S):
+    """Batches past the 64 requests one wave holds in registers (the plan then
+    reads page_indptr / kv_indptr from memory), up to the largest batch the
+    bind supports; the oracle is checked on a sample of (request, kv head)
+    pairs, the bind in full."""
+    rng = np.random.default_rng(B * 10 + S)
+    lens = [int(x) for x in np.where(rng.random(B) < 0.1, 0, rng.integers(1, 200 if B > 200 else 900, size=B))]
+    say(f"[many] B={B} sumL={sum(lens)} S={S}")
+    w = workloads.make_custom("many", seed=3000 + B + S, n_layers=1, seq_lens=lens, n_heads=8, n_kv_heads=2,
+                              head_dim=64, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w, max_splits=64)
+    ws.bind(w.batch, PD_BIND_FULL, dev.seq_lens, dev.position_ids, dev.req_to_page)
+    torch.cuda.synchronize()
+    check_bind(ws, w, w.seq_lens.numpy())
+    S_ = ws.num_splits(w.batch, S)
+    picks = sorted({int(x) for x in rng.choice(B, size=min(B, 48), replace=False)} | {0, B - 1})
+    pairs = [(b, g) for b in picks for g in range(2)]
+    check_layer(ws, w, dev, 0, S_, pairs=pairs)
+    assert ws.read_error() == 0
