@@ -25,6 +25,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-munsafe-fp-atomics"]
+# Per-source flags.  The prefill kernel's scores are never NaN (finite q, K
+# and V; masked scores are -inf), so its max reductions need no NaN
+# canonicalisation.
+FILE_FLAGS = {"prefill_attn.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:
@@ -41,7 +45,7 @@ def sources():
 
 def _compile(src: str, extra, build_dir: str) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), "-x", "hip", *COMMON, *DEVICE_FLAGS, *extra,
+    cmd = [_hipcc(), "-x", "hip", *COMMON, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra,
            "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -327,6 +327,7 @@ pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, 
   a.meta = at<int32_t>(h, h->lay.meta);
   a.claim = at<int32_t>(h, h->lay.meta) + pd::kMetaPrefillClaim;
   a.out = static_cast<uint16_t*>(d_out);
+  a.off32 = (uint64_t)layer_elems * 2 <= 0xffffffffull && (uint64_t)c.max_total_tokens * 4 <= 0xffffffffull;
   return hip_status(pd::launch_prefill(a, c.head_dim, stream));
 }
 

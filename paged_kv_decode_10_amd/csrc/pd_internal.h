@@ -154,6 +154,8 @@ struct PrefillArgs {
   int32_t* claim;             // the work-item counter (a meta word)
   uint16_t* out;              // bf16 [q_rows, n_heads, D]
   uint32_t* error_word;
+  int32_t off32;              // a layer's K (and V) store and kv_indices each span < 4 GiB:
+                              // 32-bit byte offsets from a uniform base address them
 };
 
 hipError_t launch_bind(const BindArgs& a, hipStream_t stream);

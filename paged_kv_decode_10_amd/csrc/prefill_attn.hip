@@ -278,7 +278,13 @@ struct VPiece<4> {
   __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
 };
 
-template <int D>
+// Load at a 32-bit byte offset from a wave-uniform base (one address register).
+template <typename T>
+__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
+}
+
+template <int D, bool OFF32>
 __global__ void __launch_bounds__(kThreads, PD_PREFILL_WAVES_PER_SIMD)
 prefill_lds_kernel(PrefillArgs a) {
   constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
@@ -370,7 +376,8 @@ prefill_lds_kernel(PrefillArgs a) {
       for (int m = 0; m < kPer; ++m) {
         int t = kStageTok * st + tok_of(m);
         t = t < kv_end ? t : kv_end - 1;
-        sl[m] = a.kv_indices[kv0 + t];
+        if constexpr (OFF32) sl[m] = ld_at<int32_t>(a.kv_indices, (uint32_t)(kv0 + t) * 4u);
+        else sl[m] = a.kv_indices[kv0 + t];
       }
     };
     struct Staged {
@@ -378,14 +385,29 @@ prefill_lds_kernel(PrefillArgs a) {
       VPiece<VE> v[4];
     };
     auto fetch = [&](const int32_t (&sl)[kPer], Staged& d) {
+      if constexpr (OFF32) {
+        const uint16_t* kb = a.k_layer + g * D;  // wave-uniform bases
+        const uint16_t* vb = a.v_layer + g * D;
+        const uint32_t row = (uint32_t)kv_stride * 2u;  // bytes per slot
 #pragma unroll
-      for (int m = 0; m < kKPer; ++m) {
-        const int ch = (tid + kThreads * m) % CPR;
-        d.k[m] = *reinterpret_cast<const uint4*>(a.k_layer + (int64_t)sl[m] * kv_stride + (int64_t)g * D + 8 * ch);
+        for (int m = 0; m < kKPer; ++m) {
+          const int ch = (tid + kThreads * m) % CPR;
+          d.k[m] = ld_at<uint4>(kb, (uint32_t)sl[m] * row + 16u * ch);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          d.v[i].load(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vb) +
+                                                        ((uint32_t)sl[kKPer + i] * row + 2u * VE * vc)));
+      } else {
+#pragma unroll
+        for (int m = 0; m < kKPer; ++m) {
+          const int ch = (tid + kThreads * m) % CPR;
+          d.k[m] = *reinterpret_cast<const uint4*>(a.k_layer + (int64_t)sl[m] * kv_stride + (int64_t)g * D + 8 * ch);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          d.v[i].load(a.v_layer + (int64_t)sl[kKPer + i] * kv_stride + (int64_t)g * D + VE * vc);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        d.v[i].load(a.v_layer + (int64_t)sl[kKPer + i] * kv_stride + (int64_t)g * D + VE * vc);
     };
     auto stage_to_lds = [&](int buf, const Staged& d) {
 #pragma unroll
@@ -591,10 +613,14 @@ prefill_lds_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream) {
   if (PD_PREFILL_LDS) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL(prefill_lds_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(prefill_lds_kernel<128>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+    const dim3 grid(kWavesTotal / kWaves), block(kThreads);
+    if (head_dim == 64) {
+      if (a.off32) hipLaunchKernelGGL((prefill_lds_kernel<64, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((prefill_lds_kernel<64, false>), grid, block, 0, stream, a);
+    } else {
+      if (a.off32) hipLaunchKernelGGL((prefill_lds_kernel<128, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((prefill_lds_kernel<128, false>), grid, block, 0, stream, a);
+    }
   } else {
     if (head_dim == 64)
       hipLaunchKernelGGL(prefill_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);

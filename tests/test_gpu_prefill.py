@@ -204,3 +204,38 @@ def test_extend_bind_schedule(B):
     assert np.array_equal(ws.qo_indptr[: B + 1].cpu().numpy(), want_qo)
     assert ws.req_order[:B].cpu().numpy().tolist() == order
     assert np.array_equal(ws.item_indptr[: B + 1].cpu().numpy(), want_items)
+
+
+def test_prefill_store_past_4gib():
+    """A layer store larger than 4 GiB takes the 64-bit addressing path: the
+    same K/V rows placed past the 4 GiB mark (slot + offset, page table moved
+    by the same number of pages) give the oracle's result on the compact
+    store.  (Smaller stores use 32-bit byte offsets from a uniform base.)"""
+    from paged_kv_decode_10_amd import Config, PagedDecode
+
+    say("[prefill] store past 4 GiB")
+    w = workloads.make_custom("pbig", seed=230, n_layers=1, seq_lens=[300, 45, 700], extend_lens=[60, 45, 33],
+                              n_heads=8, n_kv_heads=2, head_dim=64, page_size=16)
+    row_bytes = w.n_kv_heads * w.head_dim * 2
+    off_pages = -(-(1 << 32) // (row_bytes * w.page_size))  # pages whose rows span 4 GiB
+    off = off_pages * w.page_size
+    slots = off + w.num_slots
+    k_big = torch.empty((1, slots, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    v_big = torch.empty_like(k_big)
+    k_big[:, off:] = w.k_store.cuda()
+    v_big[:, off:] = w.v_store.cuda()
+    cfg = Config(n_layers=1, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                 page_size=w.page_size, max_batch=w.batch, max_splits=8, max_pages_per_req=w.max_pages_per_req,
+                 num_slots=slots, max_total_tokens=int(w.seq_lens.sum()))
+    ws = PagedDecode(cfg)
+    table = (w.req_to_page + off_pages).cuda().contiguous()
+    ws.bind_extend(w.batch, w.seq_lens.cuda(), w.meta["extend_lens"].cuda(), req_to_page=table)
+    q = w.q[0].cuda()
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws.prefill_attn(w.batch, 0, q, k_big, v_big, w.scale, out)
+    torch.cuda.synchronize()
+    assert ws.read_error() == 0
+    ref, _ = _oracle(w)
+    assert_close_out(out.float().cpu().numpy(), ref, "prefill past 4 GiB")
+    del k_big, v_big
+    torch.cuda.empty_cache()
