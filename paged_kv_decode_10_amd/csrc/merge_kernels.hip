@@ -132,13 +132,17 @@ merge_kernel(MergeArgs a) {
   for (int e = 0; e < E; ++e) out[e] = f32_to_bf16_rne(acc[e] * inv);
 }
 
-// Many splits (S > 64): one workgroup per (request, query head), wave k
-// taking splits [32k, 32k + 32).  Each wave requests its statistics and all
-// of its rows in one round trip, combines them relative to its own maximum,
-// and wave 0 joins the waves' sums through LDS:
+// Many splits (S > 64): kWideSlices workgroups per (request, query head),
+// each owning D / kWideSlices columns, with wave k taking splits
+// [32k, 32k + 32).  A wave requests its statistics and its splits' column
+// slices in one round trip: lanes 16-byte apart in a slice, LPS lanes per
+// split, so one load instruction covers 64 / LPS splits.  It combines them
+// relative to its own maximum, reduces over the splits a lane row holds with
+// shuffles, and wave 0 joins the waves' sums through LDS:
 //   M = max_k M_k,  out = sum_k e^(M_k - M) acc_k / sum_k e^(M_k - M) wsum_k.
 constexpr int kWideSplits = 32;  // splits per wave
 constexpr int kWideWaves = 8;    // at most 256 splits
+constexpr int kWideSlices = 4;   // column slices per head (workgroups per head); 8 measured slower
 constexpr int kWideFrom = 64;    // S above which the wide kernel is used: it reads every
                                  // split's row at once, empty ones too, which costs more
                                  // than the single wave's second round trip for fewer splits
@@ -146,25 +150,33 @@ constexpr int kWideFrom = 64;    // S above which the wide kernel is used: it re
 template <int D>
 __global__ void __launch_bounds__(kWideWaves * 64)
 merge_wide_kernel(MergeArgs a) {
-  constexpr int E = D / 64;
-  __shared__ float s_acc[kWideWaves][D];
+  constexpr int SW = D / kWideSlices;   // columns of this workgroup
+  constexpr int LPS = SW / 4;           // lanes per split (a float4 each)
+  constexpr int SPI = 64 / LPS;         // splits per load instruction
+  constexpr int NI = kWideSplits / SPI; // load instructions per wave
+  __shared__ float s_acc[kWideWaves][SW];
   __shared__ float s_m[kWideWaves], s_w[kWideWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int item = blockIdx.x;
+  const int item = blockIdx.x / kWideSlices, slice = blockIdx.x % kWideSlices;
   if (item >= active_batch(a.active, a.batch) * a.n_heads) return;  // whole workgroup
   const int64_t base = (int64_t)item * a.max_splits;
   const float* ml = a.ml_part + base * 2;
-  const float* op = a.o_part + base * D;
+  const float* op = a.o_part + base * D + slice * SW;
   const int j0 = wave * kWideSplits;
   int n = a.num_splits - j0;  // >= 1: the launch has ceil(S / 32) waves
   n = n < kWideSplits ? n : kWideSplits;
+  const int sg = lane / LPS, cq = lane % LPS;  // split within a load, column quad
   float lse = -INFINITY;
   if (lane < n) {
     const float m = ml[2 * (j0 + lane)], ln_l = ml[2 * (j0 + lane) + 1];
     lse = (m == -INFINITY) ? -INFINITY : m + ln_l;
   }
-  float v[kWideSplits][E];
-  load_rows<D, kWideSplits>(op, j0, n, lane, v);
+  float4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int jj = i * SPI + sg;
+    v[i] = *reinterpret_cast<const float4*>(op + (int64_t)(j0 + (jj < n ? jj : n - 1)) * D + 4 * cq);
+  }
   float M = lse;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
@@ -172,36 +184,46 @@ merge_wide_kernel(MergeArgs a) {
   float ws = w;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 64);
-  float acc[E];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  accumulate<D, kWideSplits>(acc, v, w, 0, n);
+  for (int i = 0; i < NI; ++i) {
+    const int jj = i * SPI + sg;
+    const float wj = __shfl(w, jj < n ? jj : 0, 64);
+    if (jj < n && wj != 0.f) {  // an empty split's row is unspecified data: never touched
+      acc.x = fmaf(wj, v[i].x, acc.x);
+      acc.y = fmaf(wj, v[i].y, acc.y);
+      acc.z = fmaf(wj, v[i].z, acc.z);
+      acc.w = fmaf(wj, v[i].w, acc.w);
+    }
+  }
+  // sum over the lanes holding the same column quad (lane bits above LPS)
 #pragma unroll
-  for (int e = 0; e < E; ++e) s_acc[wave][lane * E + e] = acc[e];
+  for (int off = LPS; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off, 64);
+    acc.y += __shfl_xor(acc.y, off, 64);
+    acc.z += __shfl_xor(acc.z, off, 64);
+    acc.w += __shfl_xor(acc.w, off, 64);
+  }
+  if (lane < LPS) *reinterpret_cast<float4*>(&s_acc[wave][4 * lane]) = acc;
   if (lane == 0) {
     s_m[wave] = M;
     s_w[wave] = ws;
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0 || lane >= SW) return;
   float Mt = -INFINITY;
   for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_m[k]);
-  float tot[E], wsum = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) tot[e] = 0.f;
+  float tot = 0.f, wsum = 0.f;
   if (Mt != -INFINITY) {
     for (int k = 0; k < nw; ++k) {
       if (s_m[k] == -INFINITY) continue;  // a wave whose splits are all empty
       const float f = __expf(s_m[k] - Mt);
       wsum = fmaf(f, s_w[k], wsum);
-#pragma unroll
-      for (int e = 0; e < E; ++e) tot[e] = fmaf(f, s_acc[k][lane * E + e], tot[e]);
+      tot = fmaf(f, s_acc[k][lane], tot);
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  uint16_t* out = a.out + (int64_t)item * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) out[e] = f32_to_bf16_rne(tot[e] * inv);
+  a.out[(int64_t)item * D + slice * SW + lane] = f32_to_bf16_rne(tot * inv);
 }
 
 }  // namespace
@@ -211,9 +233,9 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
   if (a.num_splits > kWideFrom) {
     const int waves = (a.num_splits + kWideSplits - 1) / kWideSplits;  // <= 8 (S <= 256)
     if (head_dim == 64)
-      hipLaunchKernelGGL(merge_wide_kernel<64>, dim3(items), dim3(waves * 64), 0, stream, a);
+      hipLaunchKernelGGL(merge_wide_kernel<64>, dim3(items * kWideSlices), dim3(waves * 64), 0, stream, a);
     else
-      hipLaunchKernelGGL(merge_wide_kernel<128>, dim3(items), dim3(waves * 64), 0, stream, a);
+      hipLaunchKernelGGL(merge_wide_kernel<128>, dim3(items * kWideSlices), dim3(waves * 64), 0, stream, a);
     return hipGetLastError();
   }
   dim3 grid((items + kMergeWaves - 1) / kMergeWaves);
