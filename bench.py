@@ -375,8 +375,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see the sharding note in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the split-KV path has no multi-GPU mode; requests, "
+              "kv heads or pages would shard with at most one all-gather of the split partials.",
+              file=sys.stderr)
         return 2
 
     import torch
