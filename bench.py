@@ -11,10 +11,12 @@ Prints ONE JSON line on stdout.  ``value`` is KV bytes read per second (K and
 V rows actually attended, summed over layers and steps) over the timed graph
 replays.  ``roofline`` is for the dominant kernel (the split attention),
 timed live with HIP events on its stream over a replayed graph of the 24
-attention launches.  ``cpu_baseline`` times the CPU oracle on a bounded sample
-of the same workload.  Diagnostics go to stderr.
+attention launches.  ``batch_sweep`` times one layer (attention and merge,
+caches flushed) at B = 1, 2, 4, 8, 16, 32 requests of 4096 tokens.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.  Diagnostics go to stderr.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline] [--sweep 1,2,4,8,16,32]
 """
 from __future__ import annotations
 
@@ -370,6 +372,9 @@ def main() -> int:
                          "and eager) on the 24-layer step workload; prints one JSON line")
     ap.add_argument("--oracle-budget", type=float, default=0.0,
                     help="with --configs: seconds of oracle timing per config (0 = none)")
+    ap.add_argument("--sweep", default="1,2,4,8,16,32",
+                    help="default mode: also time one layer at these batch sizes (4096 tokens each, caches "
+                         "flushed) and report them in the JSON line; empty = skip")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -539,6 +544,18 @@ def main() -> int:
         log(f"[bench] calibration copy: 3 x {n} bytes")
         del src, dst
 
+    # The metric's batch sweep: one layer per batch size, B requests of 4096
+    # tokens, each launch after a cache flush (per-launch HIP events).
+    sweep = None
+    if args.sweep:
+        rows = config_sweep([f"sweep{int(b)}" for b in args.sweep.split(",") if b], 10, 0.0, args.splits)
+        sweep = {"timing": "HIP events per launch (attn, merge), 1 GiB flush-write before each; median of 10",
+                 "seq_len": 4096, "n_heads": 32, "n_kv_heads": 8, "head_dim": 128, "page_size": 16,
+                 "rows": [{"batch": r["batch"], "num_splits": r["num_splits"], "attn_us": r["attn_us"]["median"],
+                           "merge_us": r["merge_us"]["median"], "us_per_layer": r["us_per_layer_attn_plus_merge"],
+                           "kv_gbs_attn": r["kv_gbs"], "kv_pct_of_peak_attn": r["kv_pct_of_peak"],
+                           "kv_gbs_layer": r["kv_gbs_attn_plus_merge"]} for r in rows]}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_budget, S)
@@ -561,6 +578,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if sweep is not None:
+        rec["batch_sweep"] = sweep
     print(json.dumps(rec), flush=True)
     return 0
 
