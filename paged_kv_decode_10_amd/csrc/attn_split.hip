@@ -75,15 +75,26 @@ struct VChunk<4> {  // D = 64: 8 bytes (4 bf16) of one V row per lane
   __device__ uint32_t dw(int w) const { return w == 0 ? u.x : u.y; }
 };
 
-// One 16-token unit in flight: K (A operand), V rows, and the q operand of
-// its row (loaded per unit so a row change needs no extra step).
-template <int D>
+// One 16-token unit in flight: K (A operand), V rows, and the q of its row
+// (loaded per unit so a row change needs no extra step).  The score MFMA's
+// B operand repeats the row's GP query heads over its 16 columns, so a
+// direct load would move 16/GP copies of each q byte through the vector
+// memory pipe with every unit.  Instead the row's distinct q bytes (GP heads
+// x D bf16, QCH 16-byte chunks) are read once, chunk 64j + l by lane l in
+// load j, and the operand is assembled with cross-lane permutes (QPACK).
+// With 16 heads there is no duplication to remove and each lane loads its
+// operand directly.
+template <int D, int GP>
 struct Tile {
   static constexpr int KS = D / 32;
   static constexpr int VE = D / 16;
+  static constexpr int CPH = D / 8;               // 16-byte chunks per head row
+  static constexpr int QCH = GP * CPH;            // distinct q chunks of a row
+  static constexpr int NQL = (QCH + 63) / 64;     // q loads per lane when packed
+  static constexpr bool QPACK = NQL < KS;
   uint4 k[KS];
   VChunk<VE> v[4];
-  uint4 q[KS];
+  uint4 q[QPACK ? NQL : KS];
 };
 
 // Wave-uniform description of a unit, plus the lane's slot.
@@ -206,10 +217,11 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* p) { return *p; }
 
 // With APPEND the row's newest token is read from the new-row buffer (the
 // store still holds its old contents until this launch writes them).
-template <int D, bool APPEND>
-__device__ __forceinline__ Tile<D> load_tile(const AttnArgs& a, const Unit& u, int GP, int r, int c) {
-  Tile<D> t;
-  constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
+template <int D, int GP, bool APPEND>
+__device__ __forceinline__ Tile<D, GP> load_tile(const AttnArgs& a, const Unit& u, int r, int c) {
+  using TT = Tile<D, GP>;
+  TT t;
+  constexpr int KS = TT::KS, VE = TT::VE;
   const int64_t stride = (int64_t)a.n_kv_heads * D;
   const uint16_t* kp = a.k_layer + (int64_t)u.slot * stride + (int64_t)u.g * D + 8 * r;
   if constexpr (APPEND) {
@@ -231,18 +243,61 @@ __device__ __forceinline__ Tile<D> load_tile(const AttnArgs& a, const Unit& u, i
     if constexpr (VE == 8) t.v[i].u = ld_stream(reinterpret_cast<const uint4*>(vp));
     else t.v[i].u = ld_stream(reinterpret_cast<const uint2*>(vp));
   }
-  // q of head column c (zeros past the group); the load itself is unconditional.
-  const int hq = c % GP;
-  const bool real = hq < a.group;
-  const uint16_t* qp =
-      a.q + ((int64_t)u.b * a.n_heads + (int64_t)u.g * a.group + (real ? hq : 0)) * D + 8 * r;
+  // q of the row (zeros for heads past the group); the loads are unconditional.
+  const uint16_t* qrow = a.q + ((int64_t)u.b * a.n_heads + (int64_t)u.g * a.group) * D;
+  if constexpr (TT::QPACK) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);
-    if (!real) v = make_uint4(0, 0, 0, 0);
-    t.q[s] = v;
+    for (int j = 0; j < TT::NQL; ++j) {
+      const int idx = 64 * j + 16 * r + c;  // chunk of this lane: head idx / CPH, chunk idx % CPH
+      const bool real = idx < TT::QCH && idx / TT::CPH < a.group;
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * (real ? idx : 0));
+      if (!real) v = make_uint4(0, 0, 0, 0);
+      t.q[j] = v;
+    }
+  } else {
+    // head column c, chunks r + 4s: the operand itself
+    const int hq = c % GP;
+    const bool real = hq < a.group;
+    const uint16_t* qp = qrow + (int64_t)(real ? hq : 0) * D + 8 * r;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);
+      if (!real) v = make_uint4(0, 0, 0, 0);
+      t.q[s] = v;
+    }
   }
   return t;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
+// The score MFMA's B operand for step s: lane (r, c) holds chunk r + 4s of
+// head c % GP.  In the packed layout that chunk sits in lane idx % 64 of
+// load idx / 64, idx = (c % GP) * CPH + 4s + r.
+template <int D, int GP>
+__device__ __forceinline__ uint4 q_operand(const Tile<D, GP>& T, int s, int r, int c) {
+  using TT = Tile<D, GP>;
+  if constexpr (TT::QPACK) {
+    const int idx = (c % GP) * TT::CPH + 4 * s + r;
+    const int addr = (idx & 63) * 4;  // ds_bpermute takes a byte address
+    const int j = idx >> 6;
+    uint32_t w4[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t val = 0;
+#pragma unroll
+      for (int jj = 0; jj < TT::NQL; ++jj) {
+        const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)dword_of(T.q[jj], w));
+        val = (TT::NQL == 1 || j == jj) ? x : val;
+      }
+      w4[w] = val;
+    }
+    return make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  } else {
+    return T.q[s];
+  }
 }
 
 #ifdef PD_TRACE
@@ -261,7 +316,8 @@ __device__ unsigned long long g_pd_trace[kSplitChunks * 8];
 template <int D, int GP, bool APPEND>
 __global__ void __launch_bounds__(kThreads, 2)
 split_attn_kernel(AttnArgs a) {
-  constexpr int KS = Tile<D>::KS, VE = Tile<D>::VE;
+  using TT = Tile<D, GP>;
+  constexpr int KS = TT::KS, VE = TT::VE;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // Wave index, team (= chunk) index and head within the team: wave-uniform,
@@ -424,7 +480,7 @@ split_attn_kernel(AttnArgs a) {
     }
   };
 
-  auto compute = [&](const Tile<D>& T, const Unit& u) {
+  auto compute = [&](const TT& T, const Unit& u) {
     if (u.first) reset();
     if (APPEND && u.newtok >= 0) {
       // Fused KV append: this unit holds the row's newest token, which the
@@ -457,7 +513,8 @@ split_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[s]),
-                                                   __builtin_bit_cast(bf16x8_t, T.q[s]), sc, 0, 0, 0);
+                                                   __builtin_bit_cast(bf16x8_t, q_operand(T, s, r, c)), sc, 0, 0,
+                                                   0);
     float t[4];
     bool need = false;
 #pragma unroll
@@ -506,8 +563,8 @@ split_attn_kernel(AttnArgs a) {
   Unit uB = pr.next(c);
   Unit uC = pr.next(c);
   Unit uD = pr.next(c);
-  Tile<D> TA = load_tile<D, APPEND>(a, uA, GP, r, c);
-  Tile<D> TB = load_tile<D, APPEND>(a, uB, GP, r, c);
+  TT TA = load_tile<D, GP, APPEND>(a, uA, r, c);
+  TT TB = load_tile<D, GP, APPEND>(a, uB, r, c);
   int nunits = 0;
   // The two workgroups sharing a CU: the wave arbiter favours the older one,
   // which then finishes ~20% earlier.  The later-dispatched workgroup (second
@@ -524,13 +581,13 @@ split_attn_kernel(AttnArgs a) {
       else __builtin_amdgcn_s_setprio(1);
     }
     if (nunits++ == 0) PD_STAMP(2, wall_clock64());
-    TA = load_tile<D, APPEND>(a, uC, GP, r, c);
+    TA = load_tile<D, GP, APPEND>(a, uC, r, c);
     uA = uC;
     uC = pr.next(c);
     if (!uB.valid) break;
     compute(TB, uB);
     ++nunits;
-    TB = load_tile<D, APPEND>(a, uD, GP, r, c);
+    TB = load_tile<D, GP, APPEND>(a, uD, r, c);
     uB = uD;
     uD = pr.next(c);
   }
