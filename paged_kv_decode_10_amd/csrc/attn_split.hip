@@ -21,7 +21,8 @@
 // whatever the length mix.  With S = 1 rows are not split: team t takes
 // bundle rows t, t + C, ...
 //
-// Per wave (no LDS, no barriers: the waves of a team share only the plan), the
+// Per wave (no barriers: the waves of a team share only the plan; each wave
+// has its own LDS rows for re-laying out K), the
 // pages are consumed as 16-token units (a page, or a 16-token piece of a
 // larger page) in a software pipeline that crosses row boundaries: the slots
 // of unit n+4 are requested while unit n is computed, and its K, V and q rows
@@ -29,11 +30,14 @@
 //
 // Per unit, with lane l = 16*r + c:
 //   scores  S[token][head] = K[16 x D] . Q^T[D x 16] on v_mfma_f32_16x16x32_bf16
-//           (D/32 steps).  Lane l loads token c's K row in 16-byte chunks at
-//           byte 16*r + 64*s (one instruction reads 64 contiguous bytes of 16
-//           rows) -- already the MFMA A-operand layout.  The B operand is q of
-//           the G heads of the row, replicated over the 16 columns (column c
-//           holds head c % GP).  Lane l receives tokens 4r+i, head column c.
+//           (D/32 steps).  K rows are loaded whole like V (lane l: chunk c of
+//           token 4r+i, four whole rows per instruction) and pass through the
+//           wave's LDS rows into the A-operand layout (lane l: token c, 16-byte
+//           chunks at byte 16*r + 64*s); loading that layout directly reads 64
+//           bytes per row per instruction, which gathers slower.  The B operand
+//           is q of the G heads of the row, replicated over the 16 columns
+//           (column c holds head c % GP).  Lane l receives tokens 4r+i, head
+//           column c.
 //   p       exp2(score * scale*log2(e) - mref): a per-head reference max that
 //           is only raised when a score passes it by more than kSlack (rare),
 //           so the accumulator rescale is off the common path; the exact max
@@ -92,7 +96,7 @@ struct Tile {
   static constexpr int QCH = GP * CPH;            // distinct q chunks of a row
   static constexpr int NQL = (QCH + 63) / 64;     // q loads per lane when packed
   static constexpr bool QPACK = NQL < KS;
-  uint4 k[KS];
+  VChunk<VE> k[4];  // like v: lane (r, c) holds chunk c of token 4r + i
   VChunk<VE> v[4];
   uint4 q[QPACK ? NQL : KS];
 };
@@ -223,25 +227,28 @@ __device__ __forceinline__ Tile<D, GP> load_tile(const AttnArgs& a, const Unit& 
   TT t;
   constexpr int KS = TT::KS, VE = TT::VE;
   const int64_t stride = (int64_t)a.n_kv_heads * D;
-  const uint16_t* kp = a.k_layer + (int64_t)u.slot * stride + (int64_t)u.g * D + 8 * r;
-  if constexpr (APPEND) {
-    const uint16_t* kn = a.k_new + ((int64_t)u.b * a.n_kv_heads + u.g) * D + 8 * r;
-    kp = (c == u.newtok) ? kn : kp;
-  }
-  // K and V are read exactly once: streaming (non-temporal) loads keep them
-  // from evicting the q rows and the index lists from the caches.
-#pragma unroll
-  for (int s = 0; s < KS; ++s) t.k[s] = ld_stream(reinterpret_cast<const uint4*>(kp + 32 * s));
+  // K and V rows are read whole, four tokens per instruction (lane (r, c):
+  // chunk c of token 4r + i), and exactly once: streaming (non-temporal)
+  // loads keep them from evicting the q rows and the index lists.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int32_t sv = __shfl(u.slot, 4 * r + i, 64);
-    const uint16_t* vp = a.v_layer + (int64_t)sv * stride + (int64_t)u.g * D + VE * c;
+    const int64_t off = (int64_t)sv * stride + (int64_t)u.g * D + VE * c;
+    const uint16_t* kp = a.k_layer + off;
+    const uint16_t* vp = a.v_layer + off;
     if constexpr (APPEND) {
-      const uint16_t* vn = a.v_new + ((int64_t)u.b * a.n_kv_heads + u.g) * D + VE * c;
-      vp = (4 * r + i == u.newtok) ? vn : vp;
+      const int64_t noff = ((int64_t)u.b * a.n_kv_heads + u.g) * D + VE * c;
+      const bool fresh = 4 * r + i == u.newtok;
+      kp = fresh ? a.k_new + noff : kp;
+      vp = fresh ? a.v_new + noff : vp;
     }
-    if constexpr (VE == 8) t.v[i].u = ld_stream(reinterpret_cast<const uint4*>(vp));
-    else t.v[i].u = ld_stream(reinterpret_cast<const uint2*>(vp));
+    if constexpr (VE == 8) {
+      t.k[i].u = ld_stream(reinterpret_cast<const uint4*>(kp));
+      t.v[i].u = ld_stream(reinterpret_cast<const uint4*>(vp));
+    } else {
+      t.k[i].u = ld_stream(reinterpret_cast<const uint2*>(kp));
+      t.v[i].u = ld_stream(reinterpret_cast<const uint2*>(vp));
+    }
   }
   // q of the row (zeros for heads past the group); the loads are unconditional.
   const uint16_t* qrow = a.q + ((int64_t)u.b * a.n_heads + (int64_t)u.g * a.group) * D;
@@ -318,8 +325,11 @@ __global__ void __launch_bounds__(kThreads, 2)
 split_attn_kernel(AttnArgs a) {
   using TT = Tile<D, GP>;
   constexpr int KS = TT::KS, VE = TT::VE;
+  constexpr int kRowB = 2 * D + 16;  // LDS bytes per K row (16 bytes of padding against bank conflicts)
+  __shared__ __attribute__((aligned(16))) char k_lds[kWaves * 16 * kRowB];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  char* const kl = k_lds + wave * 16 * kRowB;
   // Wave index, team (= chunk) index and head within the team: wave-uniform,
   // so the plan lives in SGPRs.
   const int T = a.team;
@@ -488,31 +498,49 @@ split_attn_kernel(AttnArgs a) {
       // during this launch).  The lanes that hold its K and V chunks store
       // them at that slot, straight from the tile's registers.
       const int64_t row = (__shfl(u.slot, u.newtok, 64) * (int64_t)a.n_kv_heads + u.g) * D;
-      if (c == u.newtok) {  // lanes 16r + newtok: 16-byte K chunks at 16r + 64s
-        uint16_t* kd = a.k_dst + row + 8 * r;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4*>(kd + 32 * s) = T.k[s];
-      }
-      if (r == (u.newtok >> 2)) {  // row group of token 4r + i: V chunk VE*c
+      if (r == (u.newtok >> 2)) {  // row group of token 4r + i: K and V chunk VE*c
         const int i = u.newtok & 3;
         auto pick = [&](uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
           return i == 0 ? x0 : i == 1 ? x1 : i == 2 ? x2 : x3;
         };
-        uint16_t* vd = a.v_dst + row + VE * c;
-        if constexpr (VE == 8) {
-          *reinterpret_cast<uint4*>(vd) = make_uint4(
-              pick(T.v[0].u.x, T.v[1].u.x, T.v[2].u.x, T.v[3].u.x), pick(T.v[0].u.y, T.v[1].u.y, T.v[2].u.y, T.v[3].u.y),
-              pick(T.v[0].u.z, T.v[1].u.z, T.v[2].u.z, T.v[3].u.z), pick(T.v[0].u.w, T.v[1].u.w, T.v[2].u.w, T.v[3].u.w));
-        } else {
-          *reinterpret_cast<uint2*>(vd) = make_uint2(pick(T.v[0].u.x, T.v[1].u.x, T.v[2].u.x, T.v[3].u.x),
-                                                     pick(T.v[0].u.y, T.v[1].u.y, T.v[2].u.y, T.v[3].u.y));
-        }
+        auto put = [&](uint16_t* d, const VChunk<VE> (&x)[4]) {
+          if constexpr (VE == 8) {
+            *reinterpret_cast<uint4*>(d) = make_uint4(
+                pick(x[0].u.x, x[1].u.x, x[2].u.x, x[3].u.x), pick(x[0].u.y, x[1].u.y, x[2].u.y, x[3].u.y),
+                pick(x[0].u.z, x[1].u.z, x[2].u.z, x[3].u.z), pick(x[0].u.w, x[1].u.w, x[2].u.w, x[3].u.w));
+          } else {
+            *reinterpret_cast<uint2*>(d) = make_uint2(pick(x[0].u.x, x[1].u.x, x[2].u.x, x[3].u.x),
+                                                      pick(x[0].u.y, x[1].u.y, x[2].u.y, x[3].u.y));
+          }
+        };
+        put(a.k_dst + row + VE * c, T.k);
+        put(a.v_dst + row + VE * c, T.v);
       }
     }
+    // K rows through this wave's LDS rows: written as loaded (lane (r, c):
+    // token 4r + i, chunk c), read back as the score MFMA's A operand (lane
+    // (r, c): token c, 16-byte chunks r + 4s).  LDS operations of one wave
+    // complete in order; the wave barrier keeps the compiler from moving the
+    // reads above the writes.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      char* dst = kl + (4 * r + i) * kRowB + c * (VE * 2);
+      if constexpr (VE == 8) *reinterpret_cast<uint4*>(dst) = T.k[i].u;
+      else *reinterpret_cast<uint2*>(dst) = T.k[i].u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint4 kk[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kk[s] = *reinterpret_cast<const uint4*>(kl + c * kRowB + (r + 4 * s) * 16);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[s]),
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
                                                    __builtin_bit_cast(bf16x8_t, q_operand(T, s, r, c)), sc, 0, 0,
                                                    0);
     float t[4];
