@@ -42,10 +42,18 @@ def log(*a):
 
 
 def attn_kernel_digest() -> str:
+    """Digest of the attention sources' code: comments and whitespace are
+    dropped, so only a change to the code itself invalidates the committed
+    counter figures."""
+    import re
+
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

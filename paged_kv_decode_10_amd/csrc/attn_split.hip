@@ -22,11 +22,11 @@
 // bundle rows t, t + C, ...
 //
 // Per wave (no barriers: the waves of a team share only the plan; each wave
-// has its own LDS rows for re-laying out K), the
-// pages are consumed as 16-token units (a page, or a 16-token piece of a
-// larger page) in a software pipeline that crosses row boundaries: the slots
-// of unit n+4 are requested while unit n is computed, and its K, V and q rows
-// two units before they are needed, so a new row costs no exposed latency.
+// has its own LDS rows for re-laying out K), the pages are consumed as
+// 16-token units (a page, or a 16-token piece of a larger page) in a software
+// pipeline that crosses row boundaries: the slots of unit n+4 are requested
+// while unit n is computed, and its K and V rows and its row's q two units
+// before they are needed, so a new row costs no exposed latency.
 //
 // Per unit, with lane l = 16*r + c:
 //   scores  S[token][head] = K[16 x D] . Q^T[D x 16] on v_mfma_f32_16x16x32_bf16
@@ -36,7 +36,8 @@
 //           chunks at byte 16*r + 64*s); loading that layout directly reads 64
 //           bytes per row per instruction, which gathers slower.  The B operand
 //           is q of the G heads of the row, replicated over the 16 columns
-//           (column c holds head c % GP).  Lane l receives tokens 4r+i, head
+//           (column c holds head c % GP), assembled by cross-lane permutes from
+//           one copy of the row's q.  Lane l receives tokens 4r+i, head
 //           column c.
 //   p       exp2(score * scale*log2(e) - mref): a per-head reference max that
 //           is only raised when a score passes it by more than kSlack (rare),
