@@ -57,17 +57,27 @@ def attn_kernel_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def row_splits(seq_lens, page_size, n_kv_heads, num_splits, chunks=2048):
-    """Splits of every (request, kv head) row under the launch's plan.  Kv
-    heads form bundles of T = gcd(n_kv_heads, 4); a bundle row of P pages
-    starting at global page G meets the chunks floor(G/Qp) .. floor((G+P-1)/Qp)
-    of 2048/T chunks (one split per non-empty row when S = 1)."""
+def plan_args(n_kv_heads):
+    """The launch's split-plan parameters: bundle size T = gcd(n_kv_heads,
+    PD_PLAN_TEAM_MAX) and chunk count C = PD_PLAN_WAVES / T."""
     import math
 
+    from paged_kv_decode_10_amd._abi import PD_PLAN_TEAM_MAX, PD_PLAN_WAVES
+
+    team = math.gcd(int(n_kv_heads), PD_PLAN_TEAM_MAX)
+    return {"n_chunks": PD_PLAN_WAVES // team, "team": team}
+
+
+def row_splits(seq_lens, page_size, n_kv_heads, num_splits):
+    """Splits of every (request, kv head) row under the launch's plan.  Kv
+    heads form bundles of T heads; a bundle row of P pages starting at global
+    page G meets the chunks floor(G/Qp) .. floor((G+P-1)/Qp) of the C chunks
+    (one split per non-empty row when S = 1)."""
     import numpy as np
 
-    team = math.gcd(n_kv_heads, 4)
-    hs, nch = n_kv_heads // team, chunks // team
+    pa = plan_args(n_kv_heads)
+    team, nch = pa["team"], pa["n_chunks"]
+    hs = n_kv_heads // team
     P = (np.asarray(seq_lens, dtype=np.int64) + page_size - 1) // page_size
     Pr = np.repeat(P[:, None], hs, axis=1)
     if num_splits == 1:
@@ -101,8 +111,9 @@ def attn_bytes(seq_lens, n_kv_heads, head_dim, batch, n_heads, num_splits, page_
 def cpu_baseline(w, budget_s: float, num_splits: int):
     """Time the oracle on the same step, layer after layer, until ~budget_s.
 
-    Per layer it computes what the GPU path produces: the bind (kv_indptr,
-    kv_indices), the per-split partials and the merged attention output.
+    Per layer it computes what the GPU path produces, the way the GPU path
+    does: the bind (kv_indptr, kv_indices), the per-split partials (one pass
+    over the layer's K and V) and their log-sum-exp merge into the output.
     """
     import numpy as np
     import torch
@@ -120,18 +131,17 @@ def cpu_baseline(w, budget_s: float, num_splits: int):
     while time.perf_counter() - t0 < budget_s:
         layer = layers % w.n_layers
         ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
-        oracle.split_partials(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix, w.scale,
-                              w.n_kv_heads, w.page_size, num_splits)
-        oracle.decode_attention(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix, w.scale,
-                                w.n_kv_heads)
+        o, _, lse = oracle.split_partials(w.q[layer], w.k_store[layer], w.v_store[layer], L, ip, ix, w.scale,
+                                          w.n_kv_heads, w.page_size, num_splits, **plan_args(w.n_kv_heads))
+        oracle.merge_splits(o, lse)
         layers += 1
         kv += int(L.sum()) * w.n_kv_heads * w.head_dim * 2 * 2
     dt = time.perf_counter() - t0
     cores = max(torch.get_num_threads(), blas)
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"float64 numpy oracle on the same decode step: {layers} layer passes (bind, "
-                      f"per-split partials with S={num_splits}, merged attention; all 32 requests x 8 kv "
-                      f"heads), {kv / 1e6:.0f} MB of KV in {dt:.1f} s; host affinity "
+                      f"per-split partials with S={num_splits}, log-sum-exp merge; all 32 requests x 8 kv "
+                      f"heads; K and V read once per pass), {kv / 1e6:.0f} MB of KV in {dt:.1f} s; host affinity "
                       f"{len(os.sched_getaffinity(0))} cpus, torch threads {torch.get_num_threads()}, "
                       f"BLAS threads {blas}; numpy {np.__version__}"}
 

@@ -42,7 +42,8 @@ extern "C" {
 
 typedef enum pd_status {
   PD_OK = 0,
-  PD_E_INVALID = 1,     /* null / misaligned pointer, bad dimension or mode   */
+  PD_E_INVALID = 1,     /* null / misaligned pointer, bad dimension or mode,
+                           a batch other than the last bind's               */
   PD_E_UNSUPPORTED = 2, /* head_dim not 64/128, n_heads % n_kv_heads != 0,
                            group size above 16 ([EX]: graphs only for a
                            supported head_dim)                                */
@@ -65,6 +66,15 @@ enum {
   PD_ERR_EXTEND_OVER_LEN = 1u << 4 /* extend bind: extend_lens[b] > seq_lens[b]
                                       (after clipping): treated as seq_lens[b] */
 };
+
+/* Launch constants of the split plan (part of the ABI: the partition that
+ * paged_decode_attn documents is defined in terms of them, and the same
+ * values hold on every device).  One attention launch runs PD_PLAN_WAVES
+ * waves (512 workgroups of 4: two per compute unit on a 256-CU MI355X); kv
+ * heads are bundled T = gcd(n_kv_heads, PD_PLAN_TEAM_MAX) at a time and the
+ * page sequence is cut into C = PD_PLAN_WAVES / T chunks. */
+#define PD_PLAN_WAVES 2048
+#define PD_PLAN_TEAM_MAX 4
 
 /* Bind modes ([CA]: steady-state detection lets bind increment seq_lens and
  * kv_indptr in place and reuse the request map; [WS]: position_ids, seq_lens
@@ -116,10 +126,15 @@ typedef struct pd_layout {
 
 typedef struct pd_handle pd_handle;
 
-/* Arena size for a config (pure host).  Every sub-buffer is 256-byte aligned. */
+/* Arena size for a config (pure host).  Every sub-buffer is 256-byte aligned.
+ * ([WS]: the workspace owns decode_o_part / decode_ml_part / decode_out and
+ * the bind metadata, all sized once at executor init; this call sizes the
+ * library's share of that workspace.) */
 pd_status paged_decode_workspace_bytes(const pd_config* cfg, size_t* bytes);
 
-/* Validates cfg and carves the caller's device arena (d_arena, arena_bytes >=
+/* ([WS]: every per-step buffer is preallocated at executor init, at a fixed
+ * address, so the decode loop allocates nothing and can be graph-captured.)
+ * Validates cfg and carves the caller's device arena (d_arena, arena_bytes >=
  * paged_decode_workspace_bytes) at fixed offsets.  Allocates only the small
  * host handle; never device memory.  The arena must stay alive and untouched
  * by the caller (except through read-only views) until destroy.  Zeroes the
@@ -127,10 +142,15 @@ pd_status paged_decode_workspace_bytes(const pd_config* cfg, size_t* bytes);
 pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena,
                                       size_t arena_bytes, pd_handle** out);
 
-/* Offsets of the arena's sub-buffers, for read-only views (tests, tools). */
+/* Offsets of the arena's sub-buffers, for read-only views (tests, tools).
+ * No passage defines this call: it exposes the [WS] workspace buffers'
+ * placement, which the pages leave to the implementation. */
 pd_status paged_decode_layout(const pd_handle* h, pd_layout* out);
 
-/* Resolves the split count S for a batch: requested > 0 is honoured (it must be
+/* No passage defines a split count: the pages name the split partials
+ * ([WS] decode_o_part / decode_ml_part) but not how many splits a request
+ * gets, so the rule below is this library's own.
+ * Resolves the split count S for a batch: requested > 0 is honoured (it must be
  * <= max_splits); requested == 0 picks S = 1 + ceil(4096 / (batch*n_kv_heads)),
  * capped at max_splits and max_pages_per_req (at least 2), so that the split
  * plan below can give all chunks the same number of pages.
@@ -169,19 +189,21 @@ pd_status paged_decode_bind_contiguous(pd_handle* h, int32_t batch, int32_t mode
  *   d_v_store  whole store; the library adds the 64-bit offset of `layer`)
  *   scale      softmax scale applied to q.k (float32)
  * Split plan (S = num_splits, P_b = ceil(L_b / page_size)): the kv heads
- * form bundles of T = gcd(n_kv_heads, 4) consecutive heads, and the bundle
- * rows (request b, bundle gs) are laid end to end, request-major, each as its
- * P_b pages.  S = 1: each row is one split.  S >= 2: the page sequence is cut
- * into chunks of Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1) pages
- * (C = 2048 / T, TP = (n_kv_heads / T) * sum P_b, P_max = max P_b), and split
+ * form bundles of T = gcd(n_kv_heads, PD_PLAN_TEAM_MAX) consecutive heads, and
+ * the bundle rows (request b, bundle gs) are laid end to end, request-major,
+ * each as its P_b pages.  S = 1: each row is one split.  S >= 2: the page
+ * sequence is cut into chunks of Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1)
+ * pages (C = PD_PLAN_WAVES / T, TP = (n_kv_heads / T) * sum P_b,
+ * P_max = max P_b), and split
  * j of row (b, g) is the intersection of bundle row (b, g / T) with the j-th
  * chunk that touches it -- a contiguous, page-aligned token range; a row
  * never has more than S splits.  For every
  * query head h of kv head g, o_part[b,h,j,:] and ml_part[b,h,j,:] describe
  * split j; splits past a row's last one are empty: ml = (-inf, -inf) and
  * o_part is left unspecified.  Reads kv_indptr / kv_indices / page_indptr
- * from the last bind.  One launch of 512 workgroups (2048 waves; the T waves
- * of a team read the T heads of one bundle over the same chunk). */
+ * from the last bind; batch must be the last bind's (else PD_E_INVALID).
+ * One launch of PD_PLAN_WAVES waves (the T waves of a team read the T heads
+ * of one bundle over the same chunk). */
 pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
                             const void* d_q, const void* d_k_store, const void* d_v_store,
                             float scale, hipStream_t stream);
@@ -198,7 +220,8 @@ pd_status paged_decode_attn(pd_handle* h, int32_t batch, int32_t layer, int32_t 
  *                      stores, written in place (the library adds the layer
  *                      offset)
  * Slots of distinct requests must differ (a valid page table).  One kernel on
- * `stream`; all pointers 16-byte aligned. */
+ * `stream`; all pointers 16-byte aligned.  batch must be the last bind's
+ * (else PD_E_INVALID). */
 pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, const void* d_k_new,
                                  const void* d_v_new, void* d_k_store, void* d_v_store, hipStream_t stream);
 
@@ -233,7 +256,9 @@ pd_status paged_decode_bind_extend(pd_handle* h, int32_t batch, int32_t* d_seq_l
  *   q_rows  rows the caller allocated in d_q and d_out: query rows at or past
  *           it (sum n_b > q_rows) are not computed and set PD_ERR_TOTAL_OVER_CAP
  *   d_out   bf16 [q_rows, n_heads, head_dim], caller-owned
- *   stores as in paged_decode_attn.  Reads the last extend bind.  One
+ *   stores as in paged_decode_attn.  Reads the last bind, which must be an
+ * extend bind of the same batch (else PD_E_INVALID; before any bind the
+ * arena holds an empty work list and nothing is computed).  One
  * persistent launch: 512 workgroups of 4 waves over work items (request,
  * kv head, 128 query rows), longest requests first. */
 pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, const void* d_q, int32_t q_rows,
@@ -244,7 +269,8 @@ pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, 
  * preallocated in the workspace):
  *   out[b,h,:] = sum_j exp(lse_j - LSE) o_j,  LSE = log sum_j exp(lse_j),
  * empty splits skipped, rounded to bf16 (nearest-even).  A request with no
- * tokens gets zeros.  d_out bf16 [batch, n_heads, head_dim], caller-owned. */
+ * tokens gets zeros.  d_out bf16 [batch, n_heads, head_dim], caller-owned.
+ * batch must be the last bind's (else PD_E_INVALID). */
 pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
                              hipStream_t stream);
 
@@ -305,13 +331,17 @@ pd_status paged_decode_graph_pool_key(const pd_graph_pool* p, int32_t index, int
 pd_status paged_decode_graph_pool_destroy(pd_graph_pool* p);
 
 /* Diagnostics, never in the hot path: synchronises `stream`, returns the
- * device error word (PD_ERR_* bits) and clears it. */
+ * device error word (PD_ERR_* bits) and clears it.  No passage defines it:
+ * the pages say nothing of error reporting; here capacity violations are
+ * recorded on the device so that nothing in a step reads device memory back. */
 pd_status paged_decode_read_error(pd_handle* h, uint32_t* flags, hipStream_t stream);
 
-/* Frees the host handle; the arena belongs to the caller. */
+/* Frees the host handle; the arena belongs to the caller.  No passage:
+ * lifetime management of this library's own handle. */
 pd_status paged_decode_destroy(pd_handle* h);
 
-/* Static description of a status code. */
+/* Static description of a status code.  No passage: this library's error
+ * reporting. */
 const char* paged_decode_strerror(int status);
 
 #ifdef __cplusplus

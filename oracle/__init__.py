@@ -26,15 +26,12 @@ from .paged_attention import (  # noqa: F401
     bind_steady,
     decode_attention,
     gather_rows,
-    kv_team,
     kv_indices,
     kv_indices_contiguous,
     kv_indptr,
     merge_splits,
     prefill_attention,
     qo_indptr,
-    SPLIT_CHUNKS,
-    TEAM_MAX,
     chunk_pages,
     split_partials,
     split_plan,

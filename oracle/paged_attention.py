@@ -16,15 +16,16 @@ bullets and print no formulas):
     there is no mask ([CA] bullets dropping decode_mask / page_table).
   * Softmax is natural-base; ``scale`` is the float32 value the kernel gets.
   * Split partition (the pages fix no rule; any partition yields the same
-    merged output).  The kv heads form bundles of T = gcd(Hkv, 4); the
-    bundle rows (request b, bundle gs) are laid end to end, request-major,
-    each as its P_b pages.  With S = 1 every non-empty row is one split.
-    With S >= 2 that page sequence is cut into chunks of
-    Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1) pages (C = 2048 / T,
-    TP = total pages of all bundle rows); split j of row (b, g) is the
-    intersection of bundle row (b, g // T) with the j-th chunk that touches
-    it.  A row then never has more than S splits, and every chunk holds the
-    same number of pages.  Splits past a row's last chunk are empty.
+    merged output).  The kv heads form bundles of T heads; the bundle rows
+    (request b, bundle gs) are laid end to end, request-major, each as its
+    P_b pages.  With S = 1 every non-empty row is one split.  With S >= 2
+    that page sequence is cut into chunks of
+    Qp = max(ceil(TP / C), ceil(P_max / (S - 1)), 1) pages (TP = total pages
+    of all bundle rows); split j of row (b, g) is the intersection of bundle
+    row (b, g // T) with the j-th chunk that touches it.  A row then never has
+    more than S splits, and every chunk holds the same number of pages.
+    Splits past a row's last chunk are empty.  C and T are parameters: the
+    caller passes the values of the launch whose partials it checks.
   * Per-layer KV append ([CA] bullets on the single-index write
     buffer[layer_id, loc] and on moving the slot bookkeeping into
     bind_tasks): the new token is already counted in seq_lens, so it is
@@ -237,40 +238,31 @@ def prefill_attention(q_rows, k_layer, v_layer, seq_lens, extend_lens, kv_ptr, i
 # decode_o_part / decode_ml_part and the split partial buffers).
 # --------------------------------------------------------------------------
 
-SPLIT_CHUNKS = 2048  # waves of the attention launch
-TEAM_MAX = 4         # at most this many kv heads share one page stream
-
-
-def kv_team(n_kv_heads):
-    """Heads per bundle: gcd(n_kv_heads, 4)."""
-    return math.gcd(int(n_kv_heads), TEAM_MAX)
-
-
 def _pages(seq_lens, page_size):
     return [-(-int(x) // page_size) for x in np.asarray(seq_lens).reshape(-1)]
 
 
-def chunk_pages(seq_lens, page_size, n_kv_heads, S, n_chunks=None, team=None):
+def chunk_pages(seq_lens, page_size, n_kv_heads, S, n_chunks, team):
     """Qp for S >= 2: max(ceil(TP / C), ceil(P_max / (S - 1)), 1), where the
-    bundle rows hold TP = (n_kv_heads / team) * sum P pages and C = 2048 / team."""
-    team = kv_team(n_kv_heads) if team is None else int(team)
-    n_chunks = SPLIT_CHUNKS // team if n_chunks is None else int(n_chunks)
+    bundle rows hold TP = (n_kv_heads / team) * sum P pages and C = n_chunks."""
     P = _pages(seq_lens, page_size)
-    tp = (n_kv_heads // team) * sum(P)
+    tp = (n_kv_heads // int(team)) * sum(P)
     p_max = max(P + [0])
-    return max(-(-tp // n_chunks), -(-p_max // (int(S) - 1)), 1)
+    return max(-(-tp // int(n_chunks)), -(-p_max // (int(S) - 1)), 1)
 
 
-def split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks=None, team=None):
+def split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks, team):
     """Token ranges of the splits: plan[b][g] = [(lo, hi), ...] indexed by j.
 
     The kv heads form bundles of ``team`` heads (gs = g // team); the bundle
     rows (b, gs) are walked in order, page by page, and a new split starts
     whenever the chunk index of the global page changes (S >= 2) or a row
-    begins.  Every head of a bundle gets its bundle row's splits.
+    begins.  Every head of a bundle gets its bundle row's splits.  The chunk
+    count C = ``n_chunks`` and the bundle size ``team`` are the caller's: the
+    partition is defined for any C >= 1 and any team dividing n_kv_heads.
     """
-    team = kv_team(n_kv_heads) if team is None else int(team)
-    assert n_kv_heads % team == 0
+    team = int(team)
+    assert n_kv_heads % team == 0 and int(n_chunks) >= 1
     hs = n_kv_heads // team
     L = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
     P = _pages(L, page_size)
@@ -293,15 +285,16 @@ def split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks=None, team=None):
 
 
 def split_partials(q_layer, k_layer, v_layer, seq_lens, indptr, indices, scale,
-                   n_kv_heads, page_size, S, pairs=None):
-    """Per-split outputs: o [B, H, S, D], m [B, H, S], lse [B, H, S] (float64).
+                   n_kv_heads, page_size, S, n_chunks, team, pairs=None):
+    """Per-split outputs: o [B, H, S, D], m [B, H, S], lse [B, H, S] (float64),
+    under split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks, team).
 
     Empty splits: o = 0, m = lse = -inf.
     """
     q = to_f64(q_layer)
     B, H, D = q.shape
     G = H // n_kv_heads
-    plan = split_plan(seq_lens, page_size, n_kv_heads, S)
+    plan = split_plan(seq_lens, page_size, n_kv_heads, S, n_chunks, team)
     o = np.full((B, H, S, D), np.nan)
     m = np.full((B, H, S), np.nan)
     lse = np.full((B, H, S), np.nan)

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_de
 
 PD_OK, PD_E_INVALID, PD_E_UNSUPPORTED, PD_E_CAPACITY, PD_E_HIP = range(5)
 PD_BIND_FULL, PD_BIND_STEADY = 0, 1
+PD_PLAN_WAVES, PD_PLAN_TEAM_MAX = 2048, 4  # the split plan's launch constants (header #defines)
 PD_ERR_NEG_SEQ_LEN = 1 << 0
 PD_ERR_SEQ_OVER_TABLE = 1 << 1
 PD_ERR_TOTAL_OVER_CAP = 1 << 2

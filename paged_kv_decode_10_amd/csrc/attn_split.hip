@@ -110,6 +110,8 @@ struct Unit {
   int row_end; // the segment ends the row: splits after it are empty
   int ntok;    // valid tokens in the unit (lanes c < ntok)
   int newtok;  // index in the unit of the row's newest token (position L - 1), else -1
+  int fresh_lo; // tokens 4r+i >= fresh_lo of the unit resolve to position L - 1 (the
+                // newest token itself, or padding lanes that read it): 16 = none
   int b, g, j;   // g: the wave's kv head
   int32_t slot;  // per lane: slot of token c (a real row of the request)
 };
@@ -188,6 +190,10 @@ struct Producer {
     // Lanes past the unit's tokens (and every lane past the end of the work)
     // read a real token of the row instead; their scores are masked.
     const int t_last = (!done && u.ntok > 0) ? tok_hi - 1 : L - 1;
+    // Which lanes end up on position L - 1: from the newest token on in the
+    // unit that holds it (the padding lanes after it read it too), and every
+    // lane of a trailing piece past the row's end (page_size > 16).
+    u.fresh_lo = done ? 16 : u.newtok >= 0 ? u.newtok : u.ntok <= 0 ? 0 : 16;
     const int t = (c < u.ntok) ? tok_lo + c : t_last;
     u.slot = kv_indices[start + t];
     u.last = 0;
@@ -220,8 +226,10 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) { return *p; }
 __device__ __forceinline__ uint2 ld_stream(const uint2* p) { return *p; }
 #endif
 
-// With APPEND the row's newest token is read from the new-row buffer (the
-// store still holds its old contents until this launch writes them).
+// With APPEND every lane that resolves to the row's newest token reads it from
+// the new-row buffer: the store still holds that slot's old contents (possibly
+// NaN) until this launch writes them, and a masked lane's p = 0 would still
+// turn a NaN V element into a NaN accumulator in the p.V MFMA.
 template <int D, int GP, bool APPEND>
 __device__ __forceinline__ Tile<D, GP> load_tile(const AttnArgs& a, const Unit& u, int r, int c) {
   using TT = Tile<D, GP>;
@@ -239,7 +247,7 @@ __device__ __forceinline__ Tile<D, GP> load_tile(const AttnArgs& a, const Unit& 
     const uint16_t* vp = a.v_layer + off;
     if constexpr (APPEND) {
       const int64_t noff = ((int64_t)u.b * a.n_kv_heads + u.g) * D + VE * c;
-      const bool fresh = 4 * r + i == u.newtok;
+      const bool fresh = 4 * r + i >= u.fresh_lo;
       kp = fresh ? a.k_new + noff : kp;
       vp = fresh ? a.v_new + noff : vp;
     }

@@ -92,17 +92,16 @@ pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena, size_
   if (!d_arena || !aligned(d_arena, kAlign)) return PD_E_INVALID;
   pd_layout lay = make_layout(cfg);
   if (arena_bytes < lay.arena_bytes) return PD_E_CAPACITY;
-  int dev = 0, cus = 0;
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PD_E_HIP;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return PD_E_HIP;
   pd_handle* h = new (std::nothrow) pd_handle;
   if (!h) return PD_E_CAPACITY;
   h->cfg = *cfg;
   h->lay = lay;
   h->arena = static_cast<char*>(d_arena);
   h->device = dev;
-  h->num_cus = cus > 0 ? cus : 256;
+  h->bound_batch = 0;
+  h->bound_extend = 0;
   // Start from an empty step: zero kv_indptr, meta and the error word so an
   // attention call before the first bind sees no tokens.
   hipError_t e = hipMemsetAsync(h->arena + lay.kv_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
@@ -192,7 +191,12 @@ pd_status pdh::bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d
     a.group = h->cfg.n_heads / h->cfg.n_kv_heads;
     a.n_kv_heads = h->cfg.n_kv_heads;
   }
-  return hip_status(pd::launch_bind(a, stream));
+  const pd_status s = hip_status(pd::launch_bind(a, stream));
+  if (s == PD_OK) {
+    h->bound_batch = batch;
+    h->bound_extend = d_extend_lens != nullptr;
+  }
+  return s;
 }
 
 extern "C" {
@@ -226,6 +230,7 @@ pd_status pdh::attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t n
   const pd_config& c = h->cfg;
   if (batch > c.max_batch || num_splits > c.max_splits || layer >= c.n_layers)
     return PD_E_CAPACITY;
+  if (!pdh::batch_matches_bind(h, batch)) return PD_E_INVALID;
   const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
   pd::AttnArgs a{};
   a.batch = batch;
@@ -278,6 +283,7 @@ pd_status paged_decode_append_kv(pd_handle* h, int32_t batch, int32_t layer, con
     return PD_E_INVALID;
   const pd_config& c = h->cfg;
   if (batch > c.max_batch || layer >= c.n_layers) return PD_E_CAPACITY;
+  if (!pdh::batch_matches_bind(h, batch)) return PD_E_INVALID;
   const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
   pd::AppendArgs a{};
   a.batch = batch;
@@ -307,6 +313,9 @@ pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, 
     return PD_E_INVALID;
   const pd_config& c = h->cfg;
   if (batch > c.max_batch || layer >= c.n_layers) return PD_E_CAPACITY;
+  // The work list (qo_indptr, item_indptr, req_order, item count) comes from
+  // an extend bind of this batch; a decode bind leaves it stale.
+  if (h->bound_batch != 0 && (!h->bound_extend || batch != h->bound_batch)) return PD_E_INVALID;
   const int64_t layer_elems = c.num_slots * c.n_kv_heads * c.head_dim;
   pd::PrefillArgs a{};
   a.batch = batch;
@@ -373,6 +382,7 @@ pd_status pdh::merge_launch(pd_handle* h, int32_t batch, int32_t num_splits, voi
   if (!h || !d_out || batch < 1 || num_splits < 1) return PD_E_INVALID;
   if (!aligned(d_out, 16)) return PD_E_INVALID;
   if (batch > h->cfg.max_batch || num_splits > h->cfg.max_splits) return PD_E_CAPACITY;
+  if (!pdh::batch_matches_bind(h, batch)) return PD_E_INVALID;
   pd::MergeArgs a{};
   a.batch = batch;
   a.active = d_active;

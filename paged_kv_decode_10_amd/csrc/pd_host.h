@@ -10,7 +10,13 @@ struct pd_handle {
   pd_layout lay;
   char* arena;
   int device;
-  int num_cus;
+  // The batch of the last bind call (0: none since init, when kv_indptr,
+  // page_indptr and the meta words are all zero and any batch reads a
+  // consistent empty step), and whether it was an extend bind.  The kernels
+  // walk page_indptr / kv_indptr up to the batch they are given, so a
+  // per-layer call must use the bound batch.
+  int32_t bound_batch;
+  int bound_extend;
 };
 
 namespace pdh {
@@ -21,6 +27,12 @@ T* at(const pd_handle* h, size_t off) {
 }
 
 inline pd_status hip_status(hipError_t e) { return e == hipSuccess ? PD_OK : PD_E_HIP; }
+
+// A per-layer call must take the batch of the last bind (any batch before the
+// first one).  Checked on the host, so it holds under graph capture too.
+inline bool batch_matches_bind(const pd_handle* h, int32_t batch) {
+  return h->bound_batch == 0 || batch == h->bound_batch;
+}
 
 int32_t auto_splits(const pd_handle* h, int32_t batch);
 

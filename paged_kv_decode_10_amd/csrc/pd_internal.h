@@ -23,10 +23,11 @@ enum MetaWord : int {
 // The attention launches this many waves.  They work in teams of
 // kv_team(n_kv_heads) waves; a team walks one chunk of the page sequence and
 // each of its waves reads one kv head of those pages.
-constexpr int kSplitChunks = 2048;
-constexpr int kTeamMax = 4;  // waves per workgroup
+constexpr int kSplitChunks = PD_PLAN_WAVES;
+constexpr int kTeamMax = PD_PLAN_TEAM_MAX;  // waves per workgroup
 
-// Waves per team = kv heads per bundle: gcd(n_kv_heads, 4).
+// Waves per team = kv heads per bundle: gcd(n_kv_heads, kTeamMax).
+static_assert(kTeamMax == 4, "kv_team below is gcd(n, 4)");
 inline __host__ __device__ int kv_team(int n_kv_heads) {
   return (n_kv_heads % 4 == 0) ? 4 : (n_kv_heads % 2 == 0) ? 2 : 1;
 }

@@ -107,3 +107,10 @@ def test_product_path_has_no_oracle_or_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "workloads" not in text or f == "build.py", f
+
+
+def test_plan_constants_match_header(abi):
+    text = open(HEADER).read()
+    for name in ("PD_PLAN_WAVES", "PD_PLAN_TEAM_MAX"):
+        m = re.search(rf"^#define\s+{name}\s+(\d+)\s*$", text, flags=re.M)
+        assert m and int(m.group(1)) == getattr(abi, name), name

@@ -6,6 +6,7 @@ import pytest
 
 import bench
 import oracle
+from tests.plan_params import plan_args
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -18,7 +19,7 @@ def test_row_splits_match_oracle_plan(seed):
     L = rng.integers(0, hi, size=B)
     S = int(rng.choice([1, 2, 3, 17, 64, 256]))
     got = bench.row_splits(L, page_size, n_kv_heads, S)
-    plan = oracle.split_plan(L, page_size, n_kv_heads, S)
+    plan = oracle.split_plan(L, page_size, n_kv_heads, S, **plan_args(n_kv_heads))
     want = np.array([[len(plan[b][g]) for g in range(n_kv_heads)] for b in range(B)])
     assert np.array_equal(got, want), (L.tolist(), page_size, n_kv_heads, S)
     assert bench.split_segments(L, page_size, n_kv_heads, S) == int(want.sum())

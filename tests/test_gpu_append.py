@@ -156,7 +156,8 @@ def test_fused_append_attn_bit_identical(hkv, D, ps, S):
     say(f"[append fused] hkv={hkv} D={D} ps={ps} S={S}")
     w = workloads.make_custom("appf", seed=50 + hkv + ps + S, n_layers=2,
                               seq_lens=[5, 0, 130, 17, 1, 64, 47, 33, 16, 32],
-                              n_heads=4 * hkv, n_kv_heads=hkv, head_dim=D, page_size=ps, growth=2)
+                              n_heads=4 * hkv, n_kv_heads=hkv, head_dim=D, page_size=ps, growth=2,
+                              nan_growth=True)
     B = w.batch
     kn, vn = _new_rows(w, 5)
     results = []
@@ -180,6 +181,7 @@ def test_fused_append_attn_bit_identical(hkv, D, ps, S):
     assert torch.equal(_bits(k0), _bits(k1)) and torch.equal(_bits(v0), _bits(v1)), "stores differ"
     assert torch.equal(m0.view(torch.int32), m1.view(torch.int32)), "partial statistics differ"
     assert torch.equal(_bits(o0), _bits(o1)), "decode_out differs"
+    assert torch.isfinite(o1.float()).all(), "stale NaN slot leaked into decode_out"
     L = w.seq_lens.numpy() + 1
     _, _, ref = _oracle_step(w, w.k_store, w.v_store, L, kn, vn, 1)
     assert_close_out(o1.float().numpy(), ref, "fused decode_out")
@@ -189,7 +191,7 @@ def test_fused_graph_step_matches_eager():
     say("[append fused] graph")
     w = workloads.make_custom("appfg", seed=46, n_layers=3,
                               seq_lens=lambda g: torch.randint(0, 500, (9,), generator=g).tolist(),
-                              n_heads=32, n_kv_heads=8, head_dim=128, page_size=16, growth=8)
+                              n_heads=32, n_kv_heads=8, head_dim=128, page_size=16, growth=8, nan_growth=True)
     B = w.batch
     kn, vn = _new_rows(w, 6)
 
@@ -231,8 +233,45 @@ def test_fused_graph_step_matches_eager():
         return outs, dev.k.cpu(), dev.v.cpu()
 
     ref, kr, vr = run(False, False)
+    assert all(torch.isfinite(o.float()).all() for o in ref)
     for fused, graph in ((True, False), (True, True)):
         got, kg, vg = run(fused, graph)
         for i, (a, b) in enumerate(zip(ref, got)):
             assert torch.equal(_bits(a), _bits(b)), f"fused={fused} graph={graph} step {i}"
         assert torch.equal(_bits(kr), _bits(kg)) and torch.equal(_bits(vr), _bits(vg))
+
+
+@pytest.mark.parametrize("ps", [1, 7, 16, 32])
+def test_fused_append_over_stale_nan_slots(ps):
+    """The slots past every request's length hold NaN (a freshly handed-out
+    page): the fused append must read the newest token only from the new-row
+    buffer, in every lane that resolves to it, and match the oracle."""
+    say(f"[append fused] stale NaN slots ps={ps}")
+    w = workloads.make_custom("appnan", seed=60 + ps, n_layers=1,
+                              seq_lens=[0, 1, ps - 1 if ps > 1 else 2, ps, ps + 1, 2 * ps - 1, 31, 33, 100],
+                              n_heads=16, n_kv_heads=4, head_dim=128, page_size=ps, growth=3, nan_growth=True)
+    B = w.batch
+    kn, vn = _new_rows(w, 7)
+    dev = to_device(w)
+    ws = make_ws(w)
+    out = torch.empty((B, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    L = w.seq_lens.numpy().astype(np.int64)
+    k_host, v_host = w.k_store[0].clone(), w.v_store[0].clone()
+    ws.bind(B, PD_BIND_FULL, dev.seq_lens, dev.position_ids, dev.req_to_page)
+    for step in range(3):
+        ws.bind(B, PD_BIND_STEADY, dev.seq_lens, dev.position_ids, dev.req_to_page)
+        L = L + 1
+        for S in (1, 3, ws.num_splits(B)):
+            ws.append_attn(B, 0, S, dev.q[0], kn[0].cuda(), vn[0].cuda(), dev.k, dev.v, w.scale)
+            ws.merge(B, S, out)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy()
+            assert np.isfinite(got).all(), f"step {step} S={S}: NaN from a stale slot"
+        slots = oracle.append_slots(L, w.req_to_page.numpy(), w.page_size)
+        k_host = oracle.append_kv(k_host, kn[0], slots)
+        v_host = oracle.append_kv(v_host, vn[0], slots)
+        assert torch.equal(_bits(dev.k[0].cpu()), _bits(k_host)) and torch.equal(_bits(dev.v[0].cpu()), _bits(v_host))
+        ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
+        ref, _ = oracle.decode_attention(w.q[0], k_host, v_host, L, ip, ix, w.scale, w.n_kv_heads)
+        assert_close_out(got, ref, f"fused decode_out over NaN slots, step {step}")
+    assert ws.read_error() == 0

@@ -2,14 +2,18 @@
 
 Every step of the pool must equal, bit for bit, the eager calls at the same
 batch with the key's split count, and leave the padding requests (batch ..
-key-1) untouched.  A pool forced to run eagerly must give the same bits.
+key-1) untouched.  A pool forced to run eagerly must give the same bits.  The
+pool's own outputs (and, with the fused append, its stores) are compared with
+the oracle after every step, at the lengths the step advanced to.
 """
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from paged_kv_decode_10_amd import PD_BIND_FULL, PD_BIND_STEADY, GraphPool
-from tests.gpu_harness import make_ws, say, to_device
+from tests.gpu_harness import assert_close_out, make_ws, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -26,17 +30,57 @@ def _bits(t):
     return t.contiguous().view(torch.int16)
 
 
-def _workload(layout="paged"):
+def _workload(layout="paged", append=False):
+    # With the fused append the slots past each length start as NaN: only the
+    # append may make them valid.
     return workloads.make_custom("pool", seed=80, n_layers=2,
                                  seq_lens=lambda g: torch.randint(1, 700, (6,), generator=g).tolist(),
-                                 n_heads=16, n_kv_heads=4, head_dim=128, page_size=16, growth=12, layout=layout)
+                                 n_heads=16, n_kv_heads=4, head_dim=128, page_size=16, growth=12, layout=layout,
+                                 nan_growth=append)
+
+
+def _new_rows_host(w, seed=9):
+    g = torch.Generator().manual_seed(seed)
+    shape = (w.n_layers, w.batch, w.n_kv_heads, w.head_dim)
+    return (torch.randn(shape, generator=g).to(torch.bfloat16),
+            torch.randn(shape, generator=g).to(torch.bfloat16))
 
 
 def _new_rows(w, seed=9):
-    g = torch.Generator().manual_seed(seed)
-    shape = (w.n_layers, w.batch, w.n_kv_heads, w.head_dim)
-    return (torch.randn(shape, generator=g).to(torch.bfloat16).cuda(),
-            torch.randn(shape, generator=g).to(torch.bfloat16).cuda())
+    k, v = _new_rows_host(w, seed)
+    return k.cuda(), v.cuda()
+
+
+class _OracleState:
+    """Host copies of the lengths and stores, advanced by the oracle."""
+
+    def __init__(self, w, append, layout):
+        self.w = w
+        self.L = w.seq_lens.numpy().astype(np.int64).copy()
+        self.k = w.k_store.clone()
+        self.v = w.v_store.clone()
+        self.kn, self.vn = _new_rows_host(w) if append else (None, None)
+        self.layout = layout
+
+    def step(self, B):
+        """A steady step of requests 0 .. B-1: their lengths +1, the new rows
+        appended (fused-append pools), then attention per layer: [layers, B, H, D]."""
+        w = self.w
+        self.L[:B] += 1
+        L = self.L[:B]
+        table = w.req_to_page.numpy()[:B]
+        ip = oracle.kv_indptr(L)
+        ix = (oracle.kv_indices_contiguous(L, w.meta["req_base"].numpy()[:B]) if self.layout == "contiguous"
+              else oracle.kv_indices(L, table, w.page_size))
+        outs = []
+        for l in range(w.n_layers):
+            if self.kn is not None:
+                slots = oracle.append_slots(L, table, w.page_size)
+                self.k[l] = oracle.append_kv(self.k[l], self.kn[l][:B], slots)
+                self.v[l] = oracle.append_kv(self.v[l], self.vn[l][:B], slots)
+            o, _ = oracle.decode_attention(w.q[l][:B], self.k[l], self.v[l], L, ip, ix, w.scale, w.n_kv_heads)
+            outs.append(o)
+        return np.stack(outs)
 
 
 class _State:
@@ -78,8 +122,9 @@ class _State:
 @pytest.mark.parametrize("append,layout", [(False, "paged"), (True, "paged"), (True, "contiguous")])
 def test_pool_steps_match_eager(append, layout):
     say(f"[pool] append={append} layout={layout}")
-    w = _workload(layout)
+    w = _workload(layout, append)
     ref, got, eag = _State(w, append, layout), _State(w, append, layout), _State(w, append, layout)
+    orc = _OracleState(w, append, layout)
     pool = got.pool()
     pool.warmup()
     keys = pool.keys()
@@ -106,6 +151,13 @@ def test_pool_steps_match_eager(append, layout):
             assert torch.equal(_bits(s.dev.k), _bits(ref.dev.k)) and torch.equal(_bits(s.dev.v), _bits(ref.dev.v))
         assert torch.equal(got.dev.seq_lens[B:], seq_before[B:]), "padding lengths were advanced"
         assert torch.equal(got.dev.seq_lens[:B], seq_before[:B] + 1)
+        # the pool's replayed (or eager) step against the oracle
+        want = orc.step(B)
+        assert got.dev.seq_lens.cpu().numpy().tolist() == orc.L.tolist()
+        assert_close_out(got.out[:, :B].double().cpu().numpy(), want, f"pool step B={B} key={key}")
+        if append:
+            assert torch.equal(_bits(got.dev.k.cpu()), _bits(orc.k)) and torch.equal(_bits(got.dev.v.cpu()),
+                                                                                     _bits(orc.v)), "stores"
     assert got.ws.read_error() == 0
     pool.close()
     eager_pool.close()

@@ -17,6 +17,7 @@ import torch
 
 import oracle
 import workloads
+from tests.plan_params import PLAN_TEAM_MAX, PLAN_WAVES, plan_args
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -305,14 +306,19 @@ def test_split_plan_golden(name):
                                  team=g["team"])
         got = [[[list(r) for r in plan[b][h]] for h in range(g["n_kv_heads"])] for b in range(2)]
         assert got == want, S
-    if g["team"] == oracle.kv_team(g["n_kv_heads"]):  # the defaults are the launch's
+    if plan_args(g["n_kv_heads"]) == {"n_chunks": g["n_chunks"], "team": g["team"]}:
+        # this example is the launch's own plan (the header's constants)
         for S, want in g["plans"].items():
-            plan = oracle.split_plan(g["seq_lens"], g["page_size"], g["n_kv_heads"], int(S))
+            plan = oracle.split_plan(g["seq_lens"], g["page_size"], g["n_kv_heads"], int(S),
+                                     **plan_args(g["n_kv_heads"]))
             assert [[[list(r) for r in plan[b][h]] for h in range(2)] for b in range(2)] == want
 
 
-def test_kv_team():
-    assert [oracle.kv_team(h) for h in (1, 2, 3, 4, 6, 8, 12, 16, 5)] == [1, 2, 1, 4, 2, 4, 4, 4, 1]
+def test_plan_constants_from_header():
+    """The bundle size is gcd(n_kv_heads, PD_PLAN_TEAM_MAX) and the chunk count PD_PLAN_WAVES / T."""
+    assert (PLAN_WAVES, PLAN_TEAM_MAX) == (2048, 4)
+    assert [plan_args(h)["team"] for h in (1, 2, 3, 4, 6, 8, 12, 16, 5)] == [1, 2, 1, 4, 2, 4, 4, 4, 1]
+    assert [plan_args(h)["n_chunks"] for h in (1, 2, 8)] == [2048, 1024, 512]
 
 
 def _brute_plan(L, ps, hkv, S, n_chunks, team):
@@ -346,7 +352,7 @@ def test_split_plan_brute_force(seed):
     ps = int(rng.choice([1, 3, 16]))
     L = [int(x) for x in rng.integers(0, 90, size=int(rng.integers(1, 6)))]
     hkv = int(rng.choice([1, 2, 3, 4, 6, 8]))
-    for team in sorted({1, oracle.kv_team(hkv)}):
+    for team in sorted({1, plan_args(hkv)["team"]}):
         for S in (1, 2, 3, 5, 9):
             for nc in (2, 7, 2048 // team):
                 got = oracle.split_plan(L, ps, hkv, S, n_chunks=nc, team=team)
@@ -367,12 +373,12 @@ def test_split_invariance_and_merge_identity(S):
     ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
     out, lse = oracle.decode_attention(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale, w.n_kv_heads)
     o, m, lsep = oracle.split_partials(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale,
-                                       w.n_kv_heads, w.page_size, S)
+                                       w.n_kv_heads, w.page_size, S, **plan_args(w.n_kv_heads))
     mo, mlse = oracle.merge_splits(o, lsep)
     np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(mlse, lse, rtol=0, atol=1e-12)
     # partition covers each (request, kv head) exactly once
-    plan = oracle.split_plan(L, w.page_size, w.n_kv_heads, S)
+    plan = oracle.split_plan(L, w.page_size, w.n_kv_heads, S, **plan_args(w.n_kv_heads))
     for b in range(w.batch):
         for g in range(w.n_kv_heads):
             rr = plan[b][g]
@@ -392,9 +398,9 @@ def test_split_partial_equals_attention_over_its_range():
     ip, ix = oracle.bind_full(L, w.req_to_page.numpy(), w.page_size)
     S = 4
     o, m, lse = oracle.split_partials(w.q[0], w.k_store[0], w.v_store[0], L, ip, ix, w.scale,
-                                      w.n_kv_heads, w.page_size, S)
+                                      w.n_kv_heads, w.page_size, S, **plan_args(w.n_kv_heads))
     G = w.group
-    plan = oracle.split_plan(L, w.page_size, w.n_kv_heads, S)
+    plan = oracle.split_plan(L, w.page_size, w.n_kv_heads, S, **plan_args(w.n_kv_heads))
     for b in range(w.batch):
         for g in range(w.n_kv_heads):
             hs = slice(g * G, (g + 1) * G)

@@ -84,7 +84,7 @@ def _fill_store(gen, n_layers, num_slots, hkv, d, chunk_rows=1 << 16):
 def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim,
                 page_size=16, num_pages=None, pool_factor=1.25, growth=0,
                 max_pages_per_req=None, q_scale=1.0, scale=None,
-                nan_unassigned=True, shuffle=True, layout="paged", extend_lens=None):
+                nan_unassigned=True, shuffle=True, layout="paged", extend_lens=None, nan_growth=False):
     """Build a workload.
 
     ``seq_lens`` is either a list of ints or a callable ``gen -> list`` that
@@ -101,6 +101,10 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
     after the lengths) makes a prefill / extend workload: request b's last
     extend_lens[b] tokens are new, and q holds one row per new token,
     [n_layers, sum(extend_lens), n_heads, head_dim], request after request.
+    ``nan_growth=True`` also fills the slots a request owns past its current
+    length (its reserved growth, and the rest of its last page) with NaN, as a
+    cache whose new pages hold stale data would: only a KV append may make
+    them valid.
     """
     gen = torch.Generator().manual_seed(seed)
     lens = list(seq_lens(gen)) if callable(seq_lens) else list(seq_lens)
@@ -155,6 +159,13 @@ def make_custom(name, *, seed, n_layers, seq_lens, n_heads, n_kv_heads, head_dim
             slot_idx = (free_pages[:, None] * page_size + torch.arange(page_size)[None, :]).flatten()
             k_store[:, slot_idx] = float("nan")
             v_store[:, slot_idx] = float("nan")
+    if nan_growth:
+        for b, pb in enumerate(pages_b):
+            pos = torch.arange(lens[b], pb * page_size)
+            if pos.numel():
+                slots = req_to_page[b, pos // page_size].long() * page_size + pos % page_size
+                k_store[:, slots] = float("nan")
+                v_store[:, slots] = float("nan")
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     seq = torch.tensor(lens, dtype=torch.int32)
