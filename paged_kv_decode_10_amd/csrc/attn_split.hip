@@ -211,7 +211,6 @@ struct Producer {
   }
 };
 
-#ifndef PD_KV_TEMPORAL
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -221,10 +220,6 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v[0], v[1]);
 }
-#else
-__device__ __forceinline__ uint4 ld_stream(const uint4* p) { return *p; }
-__device__ __forceinline__ uint2 ld_stream(const uint2* p) { return *p; }
-#endif
 
 // With APPEND every lane that resolves to the row's newest token reads it from
 // the new-row buffer: the store still holds that slot's old contents (possibly
@@ -316,19 +311,6 @@ __device__ __forceinline__ uint4 q_operand(const Tile<D, GP>& T, int s, int r, i
   }
 }
 
-#ifdef PD_TRACE
-// Profiling builds only: per-wave timestamps (100 MHz wall clock) and ids.
-__device__ unsigned long long g_pd_trace[kSplitChunks * 8];
-#define PD_STAMP(k, v)                                                            \
-  do {                                                                            \
-    if (lane == 0) g_pd_trace[(long)w * 8 + (k)] = (unsigned long long)(v);       \
-  } while (0)
-#else
-#define PD_STAMP(k, v) \
-  do {                 \
-  } while (0)
-#endif
-
 template <int D, int GP, bool APPEND>
 __global__ void __launch_bounds__(kThreads, 2)
 split_attn_kernel(AttnArgs a) {
@@ -350,7 +332,6 @@ split_attn_kernel(AttnArgs a) {
   const int Bk = a.batch;  // launch batch: bounds the per-lane index loads below
   const int B = active_batch(a.active, a.batch);
   const int Hs = Hkv / T, nch = kSplitChunks / T;
-  PD_STAMP(0, wall_clock64());
 
   // ---- this wave's first row segment ----
   // All plan inputs are fetched in one round trip: the meta words, and (for
@@ -594,7 +575,6 @@ split_attn_kernel(AttnArgs a) {
     if (u.last) finalize(u);
   };
 
-  PD_STAMP(1, wall_clock64());
   // ---- pipeline: units A, B computed alternately; C, D have slots in flight ----
   Unit uA = pr.next(c);
   Unit uB = pr.next(c);
@@ -617,7 +597,7 @@ split_attn_kernel(AttnArgs a) {
       if (young) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(1);
     }
-    if (nunits++ == 0) PD_STAMP(2, wall_clock64());
+    ++nunits;
     TA = load_tile<D, GP, APPEND>(a, uC, r, c);
     uA = uC;
     uC = pr.next(c);
@@ -629,17 +609,6 @@ split_attn_kernel(AttnArgs a) {
     uD = pr.next(c);
   }
   mark_empty_requests();
-#ifdef PD_TRACE
-  {
-    unsigned xcc;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    PD_STAMP(3, wall_clock64());
-    PD_STAMP(4, xcc);
-    PD_STAMP(5, nunits);
-  }
-#else
-  (void)nunits;
-#endif
 }
 
 template <int D, int GP>
@@ -661,16 +630,6 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-#ifdef PD_TRACE
-extern "C" int pd_trace_copy(void* dst, size_t bytes) {
-  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_pd_trace), bytes, 0, hipMemcpyDeviceToHost);
-}
-extern "C" int pd_trace_clear() {
-  static unsigned long long zeros[kSplitChunks * 8];
-  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_pd_trace), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
-}
-#endif
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t stream) {
   if (head_dim == 64) return launch_d<64>(a, stream);

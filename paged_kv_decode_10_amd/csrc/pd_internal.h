@@ -123,17 +123,10 @@ struct AppendArgs {
 };
 
 // Prefill work item: one request, one kv head, kPrefillRows query rows.  A
-// wave holds kPrefillTiles MFMA tiles of 16 (new token, query head) rows; with
-// PD_PREFILL_LDS the four waves of a workgroup share one item (and its K/V
-// tiles, staged in LDS), else each wave has an item of its own.
-#ifndef PD_PREFILL_TILES
-#define PD_PREFILL_TILES 2
-#endif
-#ifndef PD_PREFILL_LDS
-#define PD_PREFILL_LDS 1
-#endif
-constexpr int kPrefillTiles = PD_PREFILL_TILES;
-constexpr int kPrefillWavesPerItem = PD_PREFILL_LDS ? 4 : 1;
+// wave holds kPrefillTiles MFMA tiles of 16 (new token, query head) rows, and
+// the four waves of a workgroup share one item (and its K/V, staged in LDS).
+constexpr int kPrefillTiles = 2;
+constexpr int kPrefillWavesPerItem = 4;
 constexpr int kPrefillRows = 16 * kPrefillTiles * kPrefillWavesPerItem;
 
 struct PrefillArgs {

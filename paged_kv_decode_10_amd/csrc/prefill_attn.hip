@@ -7,24 +7,27 @@
 // qo_indptr); new token i sits at position p = L_b - n_b + i and attends
 // causally to the cached tokens 0 .. p of its request.
 //
-// Work item = (request b, kv head g, kPrefillRows query rows, in tiles of 16).
-// The rows of a request and kv head are its (new token i, query head hh)
-// pairs, token major, hh in [0, G): item k holds rows kPrefillRows*k .. on, so
-// each 16-row MFMA tile covers 16/G new tokens (G <= 16).  The K and V tiles
-// of a unit are loaded once for all the item's query tiles.  The launch is
-// persistent: wave w takes items w, w + 2048, ... (item_indptr, built by the
-// extend bind, gives each request's first item).  Each item walks its request's tokens 0 .. p_max in 16-token units,
-// with the decode kernel's matrix-core scheme:
+// Work item = (request b, kv head g, kPrefillRows = 128 query rows).  The
+// rows of a request and kv head are its (new token i, query head hh) pairs,
+// token major, hh in [0, G): item k holds rows 128k .. 128k + 127, so each
+// 16-row MFMA tile covers 16/G new tokens (G <= 16).  A workgroup of four
+// waves takes an item; wave wv holds the 32 rows 128k + 32wv .. as two
+// 16-row tiles, and all four share the item's K/V, which the workgroup stages
+// into LDS 64 tokens at a time.  The launch is persistent: workgroup w takes
+// item w first, then items handed out by a counter, longest requests first
+// (the extend bind orders them).  Per 64-token stage, with the decode
+// kernel's matrix-core scheme:
 //   scores  S[token][row] = K[16 x D] . Q^T[D x 16] on v_mfma_f32_16x16x32_bf16,
-//           the K rows loaded straight into the A-operand layout and the q of
-//           the 16 rows held as the B operand for the whole item;
+//           K read from LDS in the A-operand layout and the q of the tile's
+//           16 rows held as the B operand for the whole item;
 //   p       exp2 with a lazily raised reference max (rescale only when a score
 //           passes it by more than 8 in log2 units); tokens past a row's
 //           causal limit are -inf;
-//   p.V     v_mfma_f32_16x16x16_bf16 with p (bf16) as the A operand, exactly
-//           where the score MFMA left it, and the V rows packed pairwise.
-// The K/V tiles of unit u+1 and the slots of unit u+2 are in flight while
-// unit u is computed.  Outputs are normalised and rounded to bf16.
+//   p.V     v_mfma_f32_16x16x32_bf16 over two 16-token units at a time, p
+//           (bf16) as the A operand where the score MFMA left it and V staged
+//           in LDS already in the B-operand layout.
+// The next stage's K/V is fetched into registers while the current one is
+// computed.  Outputs are normalised and rounded to bf16.
 #include "pd_internal.h"
 
 namespace pd {
@@ -41,225 +44,10 @@ typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
-template <int VE>
-struct VRow;
-template <>
-struct VRow<8> {
-  uint4 u;
-  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w; }
-};
-template <>
-struct VRow<4> {
-  uint2 u;
-  __device__ uint32_t dw(int w) const { return w == 0 ? u.x : u.y; }
-};
-
-template <int D>
-struct KVTile {
-  static constexpr int KS = D / 32;
-  static constexpr int VE = D / 16;
-  uint4 k[KS];
-  VRow<VE> v[4];
-};
-
-// K rows of unit tokens (lane c: token c, chunks 16r + 64s) and V rows (lane
-// 16r + c: tokens 4r+i, chunk c), for the slot each lane c holds.
-template <int D>
-__device__ __forceinline__ KVTile<D> load_kv(const PrefillArgs& a, int32_t slot, int g, int r, int c) {
-  KVTile<D> t;
-  constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
-  const int64_t stride = (int64_t)a.n_kv_heads * D;
-  const uint16_t* kp = a.k_layer + (int64_t)slot * stride + (int64_t)g * D + 8 * r;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) t.k[s] = *reinterpret_cast<const uint4*>(kp + 32 * s);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t sv = __shfl(slot, 4 * r + i, 64);
-    const uint16_t* vp = a.v_layer + (int64_t)sv * stride + (int64_t)g * D + VE * c;
-    if constexpr (VE == 8) t.v[i].u = *reinterpret_cast<const uint4*>(vp);
-    else t.v[i].u = *reinterpret_cast<const uint2*>(vp);
-  }
-  return t;
-}
-
-#ifndef PD_PREFILL_WAVES_PER_SIMD
-#define PD_PREFILL_WAVES_PER_SIMD 2
-#endif
-
-template <int D>
-__global__ void __launch_bounds__(kThreads, PD_PREFILL_WAVES_PER_SIMD)
-prefill_kernel(PrefillArgs a) {
-  constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
-  constexpr int NQ = kPrefillTiles;
-  const int lane = threadIdx.x & 63;
-  const int r = lane >> 4, c = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
-  const int B = a.batch, G = a.group, H = a.n_heads, Hkv = a.n_kv_heads;
-  const int total_items = a.meta[kMetaTotalItems];
-
-  for (int item = w; item < total_items; item += kWavesTotal) {
-    // ---- locate the item: request b holds items [item_indptr[b], item_indptr[b+1]) ----
-    int cnt = 0;
-    for (int i0 = 0; i0 <= B; i0 += 64) {
-      const int i = i0 + lane;
-      const bool le = i <= B && a.item_indptr[i <= B ? i : B] <= item;
-      cnt += __popcll(__builtin_amdgcn_ballot_w64(le));
-    }
-    const int pos = __builtin_amdgcn_readfirstlane(cnt - 1);  // place of the request in the schedule
-    const int b = __builtin_amdgcn_readfirstlane(a.req_order[pos]);
-    const int i_lo = __builtin_amdgcn_readfirstlane(a.item_indptr[pos]);
-    const int i_hi = __builtin_amdgcn_readfirstlane(a.item_indptr[pos + 1]);
-    const int groups = (i_hi - i_lo) / Hkv;  // items per kv head
-    const int k = item - i_lo;  // the request's row groups last-first (longest causal range first)
-    const int g = k % Hkv, grp = groups - 1 - k / Hkv;
-    const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
-    const int L = __builtin_amdgcn_readfirstlane(a.kv_indptr[b + 1]) - kv0;
-    const int q0 = __builtin_amdgcn_readfirstlane(a.qo_indptr[b]);
-    const int n_all = __builtin_amdgcn_readfirstlane(a.qo_indptr[b + 1]) - q0;
-    // Query rows past the caller's q / out capacity are not computed (flagged).
-    const int n = min(n_all, max(a.q_rows - q0, 0));
-    if (n < n_all && lane == 0) atomicOr(a.error_word, PD_ERR_TOTAL_OVER_CAP);
-    if (n <= 0) continue;
-    // Tile x of the item holds rows kPrefillRows*grp + 16x + column; a row is
-    // (new token i, query head hh), token major.
-    const int row0 = kPrefillRows * grp;
-    if (row0 >= n * G) continue;  // every row of the item is past the capacity
-    const int last_tok = min(n - 1, (row0 + kPrefillRows - 1) / G);
-    const int kv_end = L - n_all + last_tok + 1;  // tokens 0 .. kv_end-1 are read
-    const int nunits = (kv_end + 15) / 16;
-
-    uint4 qv[NQ][KS];
-    int pos_c[NQ];
-#pragma unroll
-    for (int x = 0; x < NQ; ++x) {
-      const int rc = row0 + 16 * x + c;
-      const int ic = rc / G, hh = rc % G;
-      const bool valid = ic < n;
-      pos_c[x] = L - n_all + ic;  // causal limit of column c (rows past the tokens: never written)
-      const uint16_t* qp =
-          a.q + ((int64_t)(q0 + (valid ? ic : 0)) * H + (int64_t)g * G + (valid ? hh : 0)) * D + 8 * r;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * s);
-        if (!valid) v = make_uint4(0, 0, 0, 0);
-        qv[x][s] = v;
-      }
-    }
-    // Slot of token 16u + c (lanes past the range read the last token: finite
-    // data, masked below).
-    auto slot_of = [&](int u) {
-      int t = 16 * u + c;
-      t = t < kv_end ? t : kv_end - 1;
-      return a.kv_indices[kv0 + t];
-    };
-
-    f32x4_t acc[NQ][VE];
-    float mref[NQ], lsum[NQ];
-#pragma unroll
-    for (int x = 0; x < NQ; ++x) {
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[x][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mref[x] = -INFINITY;
-      lsum[x] = 0.f;
-    }
-
-    auto compute = [&](const KVTile<D>& T, int u) {
-      // V operand (shared by the tiles): element e of the four V rows, pairwise
-      u32x2_t bv[VE];
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        bv[e][0] = __builtin_amdgcn_perm(T.v[1].dw(e >> 1), T.v[0].dw(e >> 1), sel);
-        bv[e][1] = __builtin_amdgcn_perm(T.v[3].dw(e >> 1), T.v[2].dw(e >> 1), sel);
-      }
-#pragma unroll
-      for (int x = 0; x < NQ; ++x) {
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[s]),
-                                                       __builtin_bit_cast(bf16x8_t, qv[x][s]), sc, 0, 0, 0);
-        float t[4];
-        bool need = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * u + 4 * r + i;
-          t[i] = (tok <= pos_c[x] && tok < kv_end) ? sc[i] * a.scale_log2 : -INFINITY;
-          need |= t[i] > mref[x] + kSlack;
-        }
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          float cm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-          cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-          cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-          const float mnew = fmaxf(mref[x], cm);
-          const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[x] - mnew);
-          lsum[x] *= alpha;
-          mref[x] = mnew;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float ar = __shfl(alpha, 4 * r + jj, 64);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) acc[x][e][jj] *= ar;
-          }
-        }
-        bf16x4_t pb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = t[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t[i] - mref[x]);
-          lsum[x] += p;
-          pb[i] = (__bf16)p;
-        }
-        const i16x4_t pa = __builtin_bit_cast(i16x4_t, pb);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-          acc[x][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, bv[e]), acc[x][e],
-                                                                 0, 0, 0);
-      }
-    };
-
-    // ---- pipeline: tile of unit u+1 and slots of unit u+2 in flight ----
-    int32_t s_next = slot_of(nunits > 1 ? 1 : 0);
-    KVTile<D> cur = load_kv<D>(a, slot_of(0), g, r, c);
-    for (int u = 0; u < nunits; ++u) {
-      const int32_t s_after = slot_of(u + 2 < nunits ? u + 2 : nunits - 1);
-      const KVTile<D> nxt = load_kv<D>(a, s_next, g, r, c);
-      compute(cur, u);
-      cur = nxt;
-      s_next = s_after;
-    }
-
-    // ---- finalize: per column, sum over the four row groups, normalise, bf16 ----
-#pragma unroll
-    for (int x = 0; x < NQ; ++x) {
-      float l = lsum[x] + __shfl_xor(lsum[x], 16, 64);
-      l += __shfl_xor(l, 32, 64);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int col = 4 * r + jj;  // accumulator row = column
-        const float lc = __shfl(l, col, 64);
-        const int rc = row0 + 16 * x + col;
-        const int i_tok = rc / G, h_in = rc % G;
-        if (i_tok < n) {
-          const float inv = 1.0f / lc;
-          uint16_t* dst = a.out + ((int64_t)(q0 + i_tok) * H + (int64_t)g * G + h_in) * D + VE * c;
-          __bf16 ob[VE];
-#pragma unroll
-          for (int e = 0; e < VE; ++e) ob[e] = (__bf16)(acc[x][e][jj] * inv);
-          if constexpr (VE == 8) *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, ob);
-          else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, ob);
-        }
-      }
-    }
-  }
-}
-
-// Workgroup-cooperative variant: the four waves of a workgroup take the
-// item's consecutive 16*kPrefillTiles-row slices and share its K/V, which the
-// whole workgroup stages into LDS 64 tokens at a time (double buffered: stage
-// s+1 is fetched into registers while the four 16-token units of stage s are
-// computed from LDS, and the slots of stage s+2 are in flight).  Each K/V row
-// is read from memory once per item instead of once per wave, and one memory
-// round trip covers four units of compute.
+// LDS staging: double buffered (stage s+1 is fetched into registers while
+// the four 16-token units of stage s are computed from LDS, and the slots of
+// stage s+2 are in flight).  Each K/V row is read from memory once per item,
+// and one memory round trip covers four units of compute.
 constexpr int kStageTok = 64;
 
 // One token's V values for one lane column group: VE bf16 (16 or 8 bytes).
@@ -285,9 +73,10 @@ __device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
 }
 
 template <int D, bool OFF32>
-__global__ void __launch_bounds__(kThreads, PD_PREFILL_WAVES_PER_SIMD)
+__global__ void __launch_bounds__(kThreads, 2)
 prefill_lds_kernel(PrefillArgs a) {
-  constexpr int KS = KVTile<D>::KS, VE = KVTile<D>::VE;
+  constexpr int KS = D / 32;  // score MFMA steps (32 bf16 of q.k each)
+  constexpr int VE = D / 16;  // p.V accumulators (16 columns each)
   constexpr int NQ = kPrefillTiles;
   constexpr int CPR = D / 8;                          // 16-byte chunks per K or V row
   constexpr int RS = CPR + 1;                         // padded LDS row stride (uint4)
@@ -612,20 +401,13 @@ prefill_lds_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream) {
-  if (PD_PREFILL_LDS) {
-    const dim3 grid(kWavesTotal / kWaves), block(kThreads);
-    if (head_dim == 64) {
-      if (a.off32) hipLaunchKernelGGL((prefill_lds_kernel<64, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((prefill_lds_kernel<64, false>), grid, block, 0, stream, a);
-    } else {
-      if (a.off32) hipLaunchKernelGGL((prefill_lds_kernel<128, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((prefill_lds_kernel<128, false>), grid, block, 0, stream, a);
-    }
+  const dim3 grid(kWavesTotal / kWaves), block(kThreads);
+  if (head_dim == 64) {
+    if (a.off32) hipLaunchKernelGGL((prefill_lds_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_lds_kernel<64, false>), grid, block, 0, stream, a);
   } else {
-    if (head_dim == 64)
-      hipLaunchKernelGGL(prefill_kernel<64>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(prefill_kernel<128>, dim3(kWavesTotal / kWaves), dim3(kThreads), 0, stream, a);
+    if (a.off32) hipLaunchKernelGGL((prefill_lds_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_lds_kernel<128, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
