@@ -49,7 +49,9 @@ typedef enum pd_status {
                            supported head_dim)                                */
   PD_E_CAPACITY = 3,    /* batch > max_batch, splits > max_splits, arena too
                            small, layer out of range                          */
-  PD_E_HIP = 4          /* a HIP launch or copy failed                        */
+  PD_E_HIP = 4,         /* a HIP launch or copy failed                        */
+  PD_E_SCRATCH = 5      /* paged_decode_attn_merge_noalloc: the partials do not
+                           fit its 32 MiB static scratch array                */
 } pd_status;
 
 /* Bits of the device error word (see paged_decode_read_error).  A kernel that
@@ -273,6 +275,23 @@ pd_status paged_decode_prefill_attn(pd_handle* h, int32_t batch, int32_t layer, 
  * batch must be the last bind's (else PD_E_INVALID). */
 pd_status paged_decode_merge(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out,
                              hipStream_t stream);
+
+/* No-allocation variant of paged_decode_attn followed by paged_decode_merge,
+ * for callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * the same results, bit for bit, but the split partials live in a file-scope
+ * device array of the library (32 MiB per GPU, held until the process ends)
+ * instead of the workspace arena, at split stride num_splits.  The caller
+ * passes the inputs (as paged_decode_attn) and d_out (as paged_decode_merge);
+ * the arena's o_part / ml_part are not touched.  Allocates nothing, ever.
+ * Returns PD_E_SCRATCH when batch * n_heads * num_splits * (head_dim + 2) * 4
+ * bytes (o rows 256-byte aligned) exceed 32 MiB.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (other streams,
+ * handles or threads) race.  Nothing in the array needs clearing between
+ * calls: each call writes every partial statistic it reads. */
+pd_status paged_decode_attn_merge_noalloc(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits,
+                                          const void* d_q, const void* d_k_store, const void* d_v_store,
+                                          float scale, void* d_out, hipStream_t stream);
 
 /* ---- Batch-size graph pool ([EX]: graphs pre-captured at init for
  * power-of-two batch sizes, one graph per batch-size key with all inputs at

@@ -26,6 +26,7 @@ from ._abi import (  # noqa: F401
     PD_E_CAPACITY,
     PD_E_HIP,
     PD_E_INVALID,
+    PD_E_SCRATCH,
     PD_E_UNSUPPORTED,
     PD_ERR_BAD_PAGE,
     PD_ERR_EXTEND_OVER_LEN,
@@ -256,6 +257,19 @@ class PagedDecode:
         p_o = _dev_ptr(out, torch.bfloat16, "out", batch * c.n_heads * c.head_dim)
         _abi.check("paged_decode_merge",
                    _abi.lib().paged_decode_merge(self._h, batch, num_splits, p_o, _stream_ptr(stream)))
+
+    def attn_merge_noalloc(self, batch: int, layer: int, num_splits: int, q: torch.Tensor, k_store: torch.Tensor,
+                           v_store: torch.Tensor, scale: float, out: torch.Tensor, stream=None) -> None:
+        """attn() + merge() with the split partials in the library's static scratch array (no allocation)."""
+        c = self.cfg
+        store_numel = c.n_layers * c.num_slots * c.n_kv_heads * c.head_dim
+        p_q = _dev_ptr(q, torch.bfloat16, "q", batch * c.n_heads * c.head_dim)
+        p_k = _dev_ptr(k_store, torch.bfloat16, "k_store", store_numel)
+        p_v = _dev_ptr(v_store, torch.bfloat16, "v_store", store_numel)
+        p_o = _dev_ptr(out, torch.bfloat16, "out", batch * c.n_heads * c.head_dim)
+        _abi.check("paged_decode_attn_merge_noalloc",
+                   _abi.lib().paged_decode_attn_merge_noalloc(self._h, batch, layer, num_splits, p_q, p_k, p_v,
+                                                              float(scale), p_o, _stream_ptr(stream)))
 
     def read_error(self, stream=None) -> int:
         v = ctypes.c_uint32(0)

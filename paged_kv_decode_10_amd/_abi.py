@@ -13,7 +13,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library will share)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_decode.so")
 
-PD_OK, PD_E_INVALID, PD_E_UNSUPPORTED, PD_E_CAPACITY, PD_E_HIP = range(5)
+PD_OK, PD_E_INVALID, PD_E_UNSUPPORTED, PD_E_CAPACITY, PD_E_HIP, PD_E_SCRATCH = range(6)
 PD_BIND_FULL, PD_BIND_STEADY = 0, 1
 PD_PLAN_WAVES, PD_PLAN_TEAM_MAX = 2048, 4  # the split plan's launch constants (header #defines)
 PD_ERR_NEG_SEQ_LEN = 1 << 0
@@ -33,6 +33,7 @@ EXPORTS = (
     "paged_decode_append_kv",
     "paged_decode_append_attn",
     "paged_decode_merge",
+    "paged_decode_attn_merge_noalloc",
     "paged_decode_bind_extend",
     "paged_decode_prefill_attn",
     "paged_decode_graph_pool_create",
@@ -118,6 +119,7 @@ def lib() -> ctypes.CDLL:
         "paged_decode_append_kv": [P, I32, I32, P, P, P, P, P],
         "paged_decode_append_attn": [P, I32, I32, I32, P, P, P, P, P, F, P],
         "paged_decode_merge": [P, I32, I32, P, P],
+        "paged_decode_attn_merge_noalloc": [P, I32, I32, I32, P, P, P, F, P, P],
         "paged_decode_bind_extend": [P, I32, P, P, P, P, P],
         "paged_decode_prefill_attn": [P, I32, I32, P, I32, P, P, F, P, P],
         "paged_decode_graph_pool_create": [P, ctypes.POINTER(PdStepBuffers), ctypes.c_uint32, ctypes.POINTER(P)],

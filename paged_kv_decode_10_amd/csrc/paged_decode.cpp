@@ -102,6 +102,13 @@ pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena, size_
   h->device = dev;
   h->bound_batch = 0;
   h->bound_extend = 0;
+  h->scratch = nullptr;
+  // This device's static scratch array (the no-allocation entry point),
+  // looked up with the device current.
+  if (pd::scratch_address(dev, &h->scratch) != hipSuccess) {
+    delete h;
+    return PD_E_HIP;
+  }
   // Start from an empty step: zero kv_indptr, meta and the error word so an
   // attention call before the first bind sees no tokens.
   hipError_t e = hipMemsetAsync(h->arena + lay.kv_indptr, 0, (size_t)(cfg->max_batch + 1) * 4, nullptr);
@@ -221,7 +228,8 @@ pd_status paged_decode_bind_contiguous(pd_handle* h, int32_t batch, int32_t mode
 // no append) and the graph pool.
 pd_status pdh::attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
                            const void* d_k_new, const void* d_v_new, const void* d_k_store,
-                           const void* d_v_store, float scale, const int32_t* d_active, hipStream_t stream) {
+                           const void* d_v_store, float scale, const int32_t* d_active, hipStream_t stream,
+                           float* o_part, float* ml_part, int32_t part_stride) {
   if (!h || !d_q || !d_k_store || !d_v_store || batch < 1 || num_splits < 1 || layer < 0)
     return PD_E_INVALID;
   if (!aligned(d_q, 16) || !aligned(d_k_store, 16) || !aligned(d_v_store, 16))
@@ -240,7 +248,7 @@ pd_status pdh::attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t n
   a.page_size = c.page_size;
   a.num_splits = num_splits;
   a.team = pd::kv_team(c.n_kv_heads);
-  a.max_splits = c.max_splits;
+  a.max_splits = o_part ? part_stride : c.max_splits;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   a.q = static_cast<const uint16_t*>(d_q);
   a.k_layer = static_cast<const uint16_t*>(d_k_store) + (int64_t)layer * layer_elems;
@@ -249,8 +257,8 @@ pd_status pdh::attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t n
   a.kv_indices = at<int32_t>(h, h->lay.kv_indices);
   a.page_indptr = at<int32_t>(h, h->lay.page_indptr);
   a.meta = at<int32_t>(h, h->lay.meta);
-  a.o_part = at<float>(h, h->lay.o_part);
-  a.ml_part = at<float>(h, h->lay.ml_part);
+  a.o_part = o_part ? o_part : at<float>(h, h->lay.o_part);
+  a.ml_part = o_part ? ml_part : at<float>(h, h->lay.ml_part);
   a.k_new = static_cast<const uint16_t*>(d_k_new);
   a.v_new = static_cast<const uint16_t*>(d_v_new);
   a.k_dst = const_cast<uint16_t*>(a.k_layer);
@@ -371,6 +379,9 @@ const char* paged_decode_strerror(int status) {
     case PD_E_UNSUPPORTED: return "unsupported configuration (head_dim, head grouping or limits)";
     case PD_E_CAPACITY: return "capacity exceeded (batch, splits, layer or arena size)";
     case PD_E_HIP: return "HIP runtime error";
+    case PD_E_SCRATCH:
+      return "request exceeds the 32 MiB static scratch array of paged_decode_attn_merge_noalloc "
+             "(batch * n_heads * num_splits * (head_dim + 2) * 4 bytes)";
     default: return "unknown status";
   }
 }
@@ -378,7 +389,7 @@ const char* paged_decode_strerror(int status) {
 }  // extern "C"
 
 pd_status pdh::merge_launch(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out, const int32_t* d_active,
-                            hipStream_t stream) {
+                            hipStream_t stream, const float* o_part, const float* ml_part, int32_t part_stride) {
   if (!h || !d_out || batch < 1 || num_splits < 1) return PD_E_INVALID;
   if (!aligned(d_out, 16)) return PD_E_INVALID;
   if (batch > h->cfg.max_batch || num_splits > h->cfg.max_splits) return PD_E_CAPACITY;
@@ -388,9 +399,9 @@ pd_status pdh::merge_launch(pd_handle* h, int32_t batch, int32_t num_splits, voi
   a.active = d_active;
   a.n_heads = h->cfg.n_heads;
   a.num_splits = num_splits;
-  a.max_splits = h->cfg.max_splits;
-  a.o_part = at<float>(h, h->lay.o_part);
-  a.ml_part = at<float>(h, h->lay.ml_part);
+  a.max_splits = o_part ? part_stride : h->cfg.max_splits;
+  a.o_part = o_part ? o_part : at<float>(h, h->lay.o_part);
+  a.ml_part = o_part ? ml_part : at<float>(h, h->lay.ml_part);
   a.out = static_cast<uint16_t*>(d_out);
   return hip_status(pd::launch_merge(a, h->cfg.head_dim, stream));
 }

@@ -17,6 +17,7 @@ struct pd_handle {
   // per-layer call must use the bound batch.
   int32_t bound_batch;
   int bound_extend;
+  void* scratch;  // this device's static scratch array (no-allocation entry point)
 };
 
 namespace pdh {
@@ -40,11 +41,26 @@ pd_status bind_launch(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_
                       const int32_t* d_req_to_page, const int32_t* d_req_base, const int32_t* d_active,
                       hipStream_t stream, const int32_t* d_extend_lens = nullptr);
 
+// The split partials go to the arena's o_part / ml_part (split stride
+// max_splits), or, when o_part is given, to o_part / ml_part at split stride
+// part_stride (the no-allocation entry point's scratch array).
 pd_status attn_launch(pd_handle* h, int32_t batch, int32_t layer, int32_t num_splits, const void* d_q,
                       const void* d_k_new, const void* d_v_new, const void* d_k_store, const void* d_v_store,
-                      float scale, const int32_t* d_active, hipStream_t stream);
+                      float scale, const int32_t* d_active, hipStream_t stream, float* o_part = nullptr,
+                      float* ml_part = nullptr, int32_t part_stride = 0);
 
 pd_status merge_launch(pd_handle* h, int32_t batch, int32_t num_splits, void* d_out, const int32_t* d_active,
-                       hipStream_t stream);
+                       hipStream_t stream, const float* o_part = nullptr, const float* ml_part = nullptr,
+                       int32_t part_stride = 0);
+
+}  // namespace pdh
+
+namespace pd {
+// Device address of this device's static scratch array (noalloc.hip); call
+// with `device` current.
+hipError_t scratch_address(int device, void** out);
+}  // namespace pd
+
+namespace pdh {
 
 }  // namespace pdh
