@@ -229,6 +229,76 @@ def config_sweep(names, reps: int, oracle_budget: float, splits: int = 0, in_ste
     return rows
 
 
+def graph_sweep(names, reps: int, rounds: int, splits: int = 0):
+    """Per-batch attention and merge time, each launch after a cache flush,
+    measured the way a captured step runs them: three graphs of ``reps``
+    repetitions each -- [flush], [flush, attn], [flush, attn, merge] (flush =
+    a 1 GiB fill kernel) -- are replayed ``rounds`` times with HIP events
+    around each replay; attn = (T[flush, attn] - T[flush]) / reps and merge =
+    (T[flush, attn, merge] - T[flush, attn]) / reps, medians over the rounds.
+    Each kernel's time includes the boundary before it, as in the step's
+    kernel trace; no per-launch event sits between the kernels."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_decode_10_amd import PD_BIND_FULL, Config, PagedDecode
+
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    rows = []
+    for name in names:
+        w = workloads.make(name)
+        B, H, Hkv, D = w.batch, w.n_heads, w.n_kv_heads, w.head_dim
+        cfg = Config(n_layers=1, n_heads=H, n_kv_heads=Hkv, head_dim=D, page_size=w.page_size, max_batch=B,
+                     max_splits=256, max_pages_per_req=w.max_pages_per_req, num_slots=w.num_slots,
+                     max_total_tokens=int(w.seq_lens.sum()))
+        ws = PagedDecode(cfg)
+        seq, pos, tab = w.seq_lens.cuda(), w.position_ids.cuda(), w.req_to_page.cuda()
+        q, kst, vst = w.q.cuda(), w.k_store.cuda(), w.v_store.cuda()
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+        S = ws.num_splits(B, splits)
+        ws.bind(B, PD_BIND_FULL, seq, pos, tab)
+        torch.cuda.synchronize()
+
+        def capture(parts):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(reps):
+                    flush.fill_(r + 1)
+                    if "attn" in parts:
+                        ws.attn(B, 0, S, q[0], kst, vst, w.scale)
+                    if "merge" in parts:
+                        ws.merge(B, S, out)
+            return g
+
+        graphs = [capture(()), capture(("attn",)), capture(("attn", "merge"))]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = [[], [], []]
+        for rnd in range(rounds + 1):
+            for i, g in enumerate(graphs):
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                if rnd:  # the first round warms up
+                    times[i].append(e0.elapsed_time(e1) * 1e3 / reps)
+        assert ws.read_error() == 0 and torch.isfinite(out.float()).all()
+        tf, tfa, tfam = (float(np.median(t)) for t in times)
+        attn_us, merge_us = tfa - tf, tfam - tfa
+        L = w.seq_lens.to(torch.int64)
+        kv, alg = attn_bytes(L, Hkv, D, B, H, S, w.page_size)
+        rows.append({"batch": B, "num_splits": S, "attn_us": round(attn_us, 2), "merge_us": round(merge_us, 2),
+                     "us_per_layer": round(attn_us + merge_us, 2), "kv_bytes": kv,
+                     "kv_gbs_attn": round(kv / attn_us / 1e3, 1),
+                     "kv_pct_of_peak_attn": round(100 * kv / attn_us / 1e3 / HBM_PEAK_GBS, 1),
+                     "kv_gbs_layer": round(kv / (attn_us + merge_us) / 1e3, 1)})
+        log(f"[sweep] {name}: B={B} S={S} attn {attn_us:.2f} us -> {kv / attn_us / 1e3:.0f} GB/s KV "
+            f"({100 * kv / attn_us / 1e3 / HBM_PEAK_GBS:.1f}%), merge {merge_us:.2f} us (flush {tf:.1f} us)")
+        del graphs, ws, q, kst, vst
+        torch.cuda.empty_cache()
+    return rows
+
+
 def pool_sweep(batches, steps: int, warmup: int):
     """Graph pool on the 24-layer step workload: per batch size, the step time
     replaying the pool's captured graph vs the same pool run eagerly (every
@@ -563,16 +633,13 @@ def main() -> int:
         del src, dst
 
     # The metric's batch sweep: one layer per batch size, B requests of 4096
-    # tokens, each launch after a cache flush (per-launch HIP events).
+    # tokens, each launch after a cache flush, timed from graph replays.
     sweep = None
     if args.sweep:
-        rows = config_sweep([f"sweep{int(b)}" for b in args.sweep.split(",") if b], 10, 0.0, args.splits)
-        sweep = {"timing": "HIP events per launch (attn, merge), 1 GiB flush-write before each; median of 10",
-                 "seq_len": 4096, "n_heads": 32, "n_kv_heads": 8, "head_dim": 128, "page_size": 16,
-                 "rows": [{"batch": r["batch"], "num_splits": r["num_splits"], "attn_us": r["attn_us"]["median"],
-                           "merge_us": r["merge_us"]["median"], "us_per_layer": r["us_per_layer_attn_plus_merge"],
-                           "kv_gbs_attn": r["kv_gbs"], "kv_pct_of_peak_attn": r["kv_pct_of_peak"],
-                           "kv_gbs_layer": r["kv_gbs_attn_plus_merge"]} for r in rows]}
+        rows = graph_sweep([f"sweep{int(b)}" for b in args.sweep.split(",") if b], 10, 3, args.splits)
+        sweep = {"timing": "graph replays of 10 x [1 GiB flush, attn(, merge)] minus 10 x [flush], HIP events "
+                           "around each replay; median of 3 rounds",
+                 "seq_len": 4096, "n_heads": 32, "n_kv_heads": 8, "head_dim": 128, "page_size": 16, "rows": rows}
 
     cpu = None
     if not args.no_cpu_baseline:
