@@ -233,8 +233,9 @@ def graph_sweep(names, reps: int, rounds: int, splits: int = 0):
     """Per-batch attention and merge time, each launch after a cache flush,
     measured the way a captured step runs them: three graphs of ``reps``
     repetitions each -- [flush], [flush, attn], [flush, attn, merge] (flush =
-    a 1 GiB fill kernel) -- are replayed ``rounds`` times with HIP events
-    around each replay; attn = (T[flush, attn] - T[flush]) / reps and merge =
+    a 1 GiB fill kernel, four times the 256 MB Infinity Cache) -- are replayed
+    one after another ``rounds`` times with HIP events around each replay;
+    per round attn = (T[flush, attn] - T[flush]) / reps and merge =
     (T[flush, attn, merge] - T[flush, attn]) / reps, medians over the rounds.
     Each kernel's time includes the boundary before it, as in the step's
     kernel trace; no per-launch event sits between the kernels."""
@@ -283,8 +284,9 @@ def graph_sweep(names, reps: int, rounds: int, splits: int = 0):
                 if rnd:  # the first round warms up
                     times[i].append(e0.elapsed_time(e1) * 1e3 / reps)
         assert ws.read_error() == 0 and torch.isfinite(out.float()).all()
-        tf, tfa, tfam = (float(np.median(t)) for t in times)
-        attn_us, merge_us = tfa - tf, tfam - tfa
+        tf = float(np.median(times[0]))
+        attn_us = float(np.median([b - a for a, b in zip(times[0], times[1])]))
+        merge_us = float(np.median([c - b for b, c in zip(times[1], times[2])]))
         L = w.seq_lens.to(torch.int64)
         kv, alg = attn_bytes(L, Hkv, D, B, H, S, w.page_size)
         rows.append({"batch": B, "num_splits": S, "attn_us": round(attn_us, 2), "merge_us": round(merge_us, 2),
@@ -636,9 +638,9 @@ def main() -> int:
     # tokens, each launch after a cache flush, timed from graph replays.
     sweep = None
     if args.sweep:
-        rows = graph_sweep([f"sweep{int(b)}" for b in args.sweep.split(",") if b], 10, 3, args.splits)
-        sweep = {"timing": "graph replays of 10 x [1 GiB flush, attn(, merge)] minus 10 x [flush], HIP events "
-                           "around each replay; median of 3 rounds",
+        rows = graph_sweep([f"sweep{int(b)}" for b in args.sweep.split(",") if b], 20, 7, args.splits)
+        sweep = {"timing": "graph replays of 20 x [1 GiB flush, attn(, merge)] minus 20 x [flush], HIP events "
+                           "around each replay; median over 7 rounds of the per-round differences",
                  "seq_len": 4096, "n_heads": 32, "n_kv_heads": 8, "head_dim": 128, "page_size": 16, "rows": rows}
 
     cpu = None
