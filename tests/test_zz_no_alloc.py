@@ -5,7 +5,9 @@ Its decode_out must equal that of paged_decode_attn + paged_decode_merge bit
 for bit (same kernels, same partials), on two calls in a row where the second
 has a smaller input (the array keeps the first call's contents), with no
 device allocation during the calls; both also match the oracle.  A request
-whose partials do not fit the array is rejected on the host.
+whose partials do not fit the array is rejected on the host.  Captured in a
+graph (the callers it is for), every replay equals attn + merge on the same
+inputs, bit for bit.
 """
 import numpy as np
 import pytest
@@ -81,3 +83,36 @@ def test_noalloc_rejects_oversize_on_host():
     assert torch.all(out == 0)
     # 3 requests fit (25.6 MB)
     assert np.ceil(3 * 64 * 256 * 128 * 4 / 256) * 256 + 3 * 64 * 256 * 8 <= 32 << 20
+
+
+def test_noalloc_under_graph_capture():
+    w = workloads.make_custom("nag", seed=91, n_layers=2,
+                              seq_lens=lambda g: torch.randint(1, 900, (7,), generator=g).tolist(),
+                              n_heads=32, n_kv_heads=8, head_dim=128, page_size=16)
+    dev = to_device(w)
+    ws = make_ws(w, max_splits=64)
+    B = w.batch
+    S = ws.num_splits(B)
+    say(f"[noalloc graph] B={B} S={S}")
+    ws.bind(B, PD_BIND_FULL, dev.seq_lens, dev.position_ids, dev.req_to_page)
+    q = dev.q[1].clone()
+    out = torch.empty((B, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    ref = torch.empty_like(out)
+    ws.attn_merge_noalloc(B, 1, S, q, dev.k, dev.v, w.scale, out)  # live run before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ws.attn_merge_noalloc(B, 1, S, q, dev.k, dev.v, w.scale, out)
+    gen = torch.Generator().manual_seed(5)
+    for i in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen).to(torch.bfloat16).cuda())  # next step's queries
+        a0 = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_stats().get("allocation.all.allocated", 0) == a0
+        ws.attn(B, 1, S, q, dev.k, dev.v, w.scale)
+        ws.merge(B, S, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref)), f"replay {i}"
+        _ = float(out.float().abs().sum())  # eager work between replays
+    assert ws.read_error() == 0
