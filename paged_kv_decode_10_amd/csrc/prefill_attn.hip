@@ -79,11 +79,14 @@ prefill_lds_kernel(PrefillArgs a) {
   constexpr int VE = D / 16;  // p.V accumulators (16 columns each)
   constexpr int NQ = kPrefillTiles;
   constexpr int CPR = D / 8;                          // 16-byte chunks per K or V row
-  constexpr int RS = CPR + 1;                         // padded LDS row stride (uint4)
+  constexpr int RS = CPR;                             // LDS row stride (uint4), chunks XOR-swizzled by token
   constexpr int kStageChunks = kStageTok * CPR;       // K chunks per stage
   constexpr int kKPer = kStageChunks / kThreads;      // K chunks a thread moves per stage
   constexpr int kPer = kKPer + 4;                     // slots a thread needs per stage (K chunks, 4 V tokens)
-  // K: [token][chunk], rows padded.  V: transposed for the p.V operand --
+  // K: [token][chunk], 16-byte chunk k of token t stored at position k ^ (t % CPR)
+  // of the token's row (an XOR swizzle: the score reads, 16 tokens x one chunk
+  // per instruction, hit 16 different bank groups; rows padded by 16 bytes
+  // instead measured 3x the bank-conflict cycles).  V: transposed for the p.V operand --
   // word (pair p, element e, lane 16r + c) holds element e of lane column
   // group c for tokens 4r..4r+3 of the pair's first unit, then of its second
   // (eight bf16, the B operand of one 16x16x32 MFMA), written at staging.
@@ -202,7 +205,7 @@ prefill_lds_kernel(PrefillArgs a) {
 #pragma unroll
       for (int m = 0; m < kKPer; ++m) {
         const int idx = tid + kThreads * m;
-        sK[buf][(idx / CPR) * RS + idx % CPR] = d.k[m];
+        sK[buf][(idx / CPR) * RS + ((idx % CPR) ^ ((idx / CPR) & (CPR - 1)))] = d.k[m];
       }
       // element e of tokens (4vr, 4vr+1) and (4vr+2, 4vr+3), paired by byte permutes
       uint2* vt = reinterpret_cast<uint2*>(sVt[buf]);
@@ -241,7 +244,7 @@ prefill_lds_kernel(PrefillArgs a) {
       for (int uu = 0; uu < 4; ++uu) {
         uint4 kk[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kk[s] = sK[buf][(16 * uu + c) * RS + r + 4 * s];  // token c of unit uu
+        for (int s = 0; s < KS; ++s) kk[s] = sK[buf][(16 * uu + c) * RS + ((r + 4 * s) ^ ((16 * uu + c) & (CPR - 1)))];  // token c of unit uu
 #pragma unroll
         for (int x = 0; x < NQ; ++x) t[uu][x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
