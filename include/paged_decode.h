@@ -140,7 +140,11 @@ pd_status paged_decode_workspace_bytes(const pd_config* cfg, size_t* bytes);
  * paged_decode_workspace_bytes) at fixed offsets.  Allocates only the small
  * host handle; never device memory.  The arena must stay alive and untouched
  * by the caller (except through read-only views) until destroy.  Zeroes the
- * error word with a blocking copy on the null stream. */
+ * step metadata (kv_indptr, page_indptr, the extend-bind arrays, the meta
+ * words) and the error word on the null stream and waits for it, so a call
+ * before the first bind sees an empty step; looks up this device's static
+ * scratch array (paged_decode_attn_merge_noalloc) with the device current;
+ * PD_E_HIP if either fails. */
 pd_status paged_decode_init_workspace(const pd_config* cfg, void* d_arena,
                                       size_t arena_bytes, pd_handle** out);
 
@@ -167,7 +171,8 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t req
  *                   be NULL in PD_BIND_FULL)
  *   d_req_to_page   int32 [batch, max_pages_per_req] row-major page ids
  * Writes the arena's kv_indptr [batch+1] and kv_indices [sum seq_lens] and the
- * meta words.  Two kernels on `stream`; no host sync. */
+ * meta words, and makes `batch` the batch of the per-layer calls that follow.
+ * Two kernels on `stream`; no host sync. */
 pd_status paged_decode_bind(pd_handle* h, int32_t batch, int32_t mode, int32_t* d_seq_lens,
                             int32_t* d_position_ids, const int32_t* d_req_to_page,
                             hipStream_t stream);
