@@ -334,8 +334,10 @@ split_attn_kernel(AttnArgs a) {
   const int Hs = Hkv / T, nch = kSplitChunks / T;
 
   // ---- this wave's first row segment ----
-  // All plan inputs are fetched in one round trip: the meta words, and (for
-  // the first 64 requests) page_indptr and kv_indptr, held one per lane.
+  // All plan inputs are fetched in one round trip: the max-pages meta word,
+  // and (for the first 64 requests) page_indptr and kv_indptr, held one per
+  // lane.  The total page count is page_indptr[B] itself, so the chunks never
+  // reach past the requests this launch walks.
   Producer pr;
   pr.B = B; pr.Hs = Hs; pr.ps = a.page_size; pr.S = S; pr.w = tm;
   pr.nch = nch; pr.team = T; pr.member = member;
@@ -348,12 +350,13 @@ split_attn_kernel(AttnArgs a) {
   const int i_lane = lane <= Bk ? lane : Bk;  // entries past B are never used
   const int32_t pi_lane = a.page_indptr[i_lane];
   const int32_t ki_lane = a.kv_indptr[i_lane];
-  const int32_t total_pages = a.meta[kMetaTotalPages];
+  // page_indptr / kv_indptr of request bb, a wave-uniform index (read from
+  // lane bb's register when bb < 64)
+  auto pi_of = [&](int bb) { return bb < 64 ? __builtin_amdgcn_readlane(pi_lane, bb) : a.page_indptr[bb]; };
+  auto ki_of = [&](int bb) { return bb < 64 ? __builtin_amdgcn_readlane(ki_lane, bb) : a.kv_indptr[bb]; };
+  const int32_t total_pages = __builtin_amdgcn_readfirstlane(pi_of(B));
   const int32_t max_pages = a.meta[kMetaMaxPages];
   const int64_t TP = (int64_t)Hs * total_pages;
-  // page_indptr / kv_indptr of request bb (from the lane registers when bb < 64)
-  auto pi_of = [&](int bb) { return bb < 64 ? __shfl(pi_lane, bb, 64) : a.page_indptr[bb]; };
-  auto ki_of = [&](int bb) { return bb < 64 ? __shfl(ki_lane, bb, 64) : a.kv_indptr[bb]; };
   bool active = true;
   if (row_mode) {
     pr.Qp = 1; pr.p1 = 0;
