@@ -335,8 +335,9 @@ pd_status paged_decode_graph_pool_create(pd_handle* h, const pd_step_buffers* bu
 /* Captures the step of every key:
  *   steady bind, then per layer l: attention (append_attn with k_new/v_new
  *   layer l, else attn) of q layer l, and the merge into out layer l.
- * Capture executes nothing, so the buffers are not touched.  A key whose
- * capture or instantiation fails runs eagerly afterwards (see _key). */
+ * Capture executes nothing, so the buffers are not touched and the handle
+ * keeps the bind it had.  A key whose capture or instantiation fails runs
+ * eagerly afterwards (see _key). */
 pd_status paged_decode_graph_pool_warmup(pd_graph_pool* p);
 
 /* One steady decode step of requests 0 .. batch-1 (1 <= batch <= max_batch) on
@@ -344,7 +345,8 @@ pd_status paged_decode_graph_pool_warmup(pd_graph_pool* p);
  * replays (or runs eagerly) the step of the smallest key >= batch.  Every
  * kernel stops at `batch` requests: the padding requests batch .. key-1 keep
  * their lengths and their output rows.  The results equal those of the eager
- * calls with the same batch and the key's split count, bit for bit. */
+ * calls with the same batch and the key's split count, bit for bit.  Counts
+ * as a bind of `batch` requests: per-layer calls made after it take `batch`. */
 pd_status paged_decode_graph_pool_step(pd_graph_pool* p, int32_t batch, hipStream_t stream);
 
 pd_status paged_decode_graph_pool_num_keys(const pd_graph_pool* p, int32_t* n_keys);

@@ -113,6 +113,11 @@ pd_status paged_decode_graph_pool_warmup(pd_graph_pool* p) {
   if (!p) return PD_E_INVALID;
   release_graphs(p);
   if (p->flags & PD_POOL_EAGER) return PD_OK;
+  // Capturing runs the host side of every launch, which records each key's
+  // bind as the handle's bound batch; nothing reaches the device, so the
+  // handle keeps the bind it had.
+  const int32_t bound_batch = p->h->bound_batch;
+  const int bound_extend = p->h->bound_extend;
   for (int i = 0; i < p->n_keys; ++i) {
     hipGraph_t g = nullptr;
     if (hipStreamBeginCapture(p->capture_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) continue;
@@ -125,6 +130,8 @@ pd_status paged_decode_graph_pool_warmup(pd_graph_pool* p) {
     if (g) (void)hipGraphDestroy(g);
     (void)hipGetLastError();  // a failed key runs eagerly; clear its error
   }
+  p->h->bound_batch = bound_batch;
+  p->h->bound_extend = bound_extend;
   return PD_OK;
 }
 
@@ -135,8 +142,14 @@ pd_status paged_decode_graph_pool_step(pd_graph_pool* p, int32_t batch, hipStrea
   while (p->keys[i] < batch) ++i;
   hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(1), 0, stream, p->active, batch);
   if (hipGetLastError() != hipSuccess) return PD_E_HIP;
-  if (p->exec[i]) return pdh::hip_status(hipGraphLaunch(p->exec[i], stream));
-  return launch_step(p, i, stream);
+  const pd_status s = p->exec[i] ? pdh::hip_status(hipGraphLaunch(p->exec[i], stream)) : launch_step(p, i, stream);
+  // The step's bind covers requests 0 .. batch-1 (the active word): those are
+  // what a per-layer call made after it may walk.
+  if (s == PD_OK) {
+    p->h->bound_batch = batch;
+    p->h->bound_extend = 0;
+  }
+  return s;
 }
 
 pd_status paged_decode_graph_pool_num_keys(const pd_graph_pool* p, int32_t* n_keys) {

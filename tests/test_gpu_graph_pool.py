@@ -161,3 +161,44 @@ def test_pool_steps_match_eager(append, layout):
     assert got.ws.read_error() == 0
     pool.close()
     eager_pool.close()
+
+
+def test_per_layer_calls_after_pool_steps():
+    """The pool keeps the handle's record of the bound batch in step with what
+    the device holds: warmup (capture only) leaves the bind it found, and a
+    step of `batch` requests binds exactly those, so per-layer calls made
+    after it take that batch (and reproduce the step's own outputs bit for
+    bit) and any other batch is rejected on the host."""
+    from paged_kv_decode_10_amd import PD_E_INVALID, PagedDecodeError
+
+    say("[pool] per-layer calls after pool steps")
+    w = _workload()
+    st = _State(w, append=False, layout="paged")  # bound: a full bind of all 6 requests
+    pool = st.pool()
+    pool.warmup()
+    keys = {k: s for k, s, _ in pool.keys()}
+    d = st.dev
+
+    def rejected(fn):
+        with pytest.raises(PagedDecodeError) as e:
+            fn()
+        assert e.value.status == PD_E_INVALID
+
+    out = torch.full((w.batch, w.n_heads, w.head_dim), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    rejected(lambda: st.ws.attn(4, 0, keys[4], d.q[0][:4], d.k, d.v, w.scale))  # still the full bind of 6
+    st.ws.attn(w.batch, 0, keys[6], d.q[0], d.k, d.v, w.scale)
+    st.ws.merge(w.batch, keys[6], out)
+    for B in (3, 5, 1):
+        key = min(k for k in keys if k >= B)
+        pool.step(B)
+        torch.cuda.synchronize()
+        rejected(lambda: st.ws.attn(key, 0, keys[key], d.q[0][:key], d.k, d.v, w.scale) if key != B else
+                 st.ws.merge(B + 1, keys[key], out[:B + 1]))
+        for layer in range(w.n_layers):
+            out.fill_(SENTINEL)
+            st.ws.attn(B, layer, keys[key], d.q[layer][:B], d.k, d.v, w.scale)
+            st.ws.merge(B, keys[key], out[:B])
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(out[:B]), _bits(st.out[layer, :B])), f"B={B} layer={layer}"
+    assert st.ws.read_error() == 0
+    pool.close()
