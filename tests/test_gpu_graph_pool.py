@@ -119,7 +119,7 @@ class _State:
                          k_new=self.kn, v_new=self.vn, eager=eager)
 
 
-@pytest.mark.parametrize("append,layout", [(False, "paged"), (True, "paged"), (True, "contiguous")])
+@pytest.mark.parametrize("append,layout", [(False, "paged"), (False, "contiguous"), (True, "paged"), (True, "contiguous")])
 def test_pool_steps_match_eager(append, layout):
     say(f"[pool] append={append} layout={layout}")
     w = _workload(layout, append)

@@ -59,7 +59,7 @@ def test_tiny_auto_splits():
 
 @pytest.mark.parametrize("G,hkv,D,ps", [(1, 4, 128, 16), (2, 2, 64, 16), (3, 2, 128, 16), (4, 8, 128, 16),
                                         (5, 2, 64, 8), (8, 8, 128, 16), (8, 1, 64, 32), (16, 2, 128, 16),
-                                        (4, 2, 128, 1), (4, 2, 64, 7)])
+                                        (16, 1, 64, 16), (6, 4, 128, 3), (4, 2, 128, 1), (4, 2, 64, 7)])
 @pytest.mark.parametrize("S", [1, 5])
 def test_grouping_and_page_sizes(G, hkv, D, ps, S):
     say(f"[shape] G={G} hkv={hkv} D={D} ps={ps} S={S}")
